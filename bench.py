@@ -1,0 +1,277 @@
+"""Benchmark of the BSR attention hot path on one MI355X.
+
+A step is one run() of the persistent kernel over one batch of synthetic input
+(plan done beforehand; its host time is reported separately, since one plan
+serves every layer of a generation step).  Each timed step is preceded, outside
+the timed window, by a write of a 1 GiB buffer that evicts L2 and the 256 MB
+Infinity Cache, and is timed with HIP events on the stream the kernel runs on.
+
+The headline line is the batch decode workload (64 requests, KV 512..8192,
+Llama-3-8B attention shape): achieved HBM bandwidth = algorithmic bytes / median
+step time.  The other workloads are reported in "workloads" (decode: TB/s;
+prefill: TFLOP/s).  The CPU oracle is timed on the same host as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn HBM TB/s (% peak) + ragged prefill TFLOPS (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+HEADLINE = "batch_decode"
+ALL = ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill", "shared_prefix_composable"]
+
+
+def algorithmic_work(w, composable=False):
+    """Bytes the method must move and flops it must do (masked pairs excluded)."""
+    elt = 2 if w.dtype == "bf16" else 4
+    h_qo, h_kv, d = w.num_qo_heads, w.num_kv_heads, w.head_dim
+    total_qo = int(w.qo_indptr[-1])
+    qol = w.qo_lens.astype(np.int64)
+    if composable:
+        keys = 0
+        pages = 0
+        for f in w.formats:
+            n = np.diff(f.kv_indptr.astype(np.int64))
+            lens = np.where(n > 0, (n - 1) * w.page_size + f.last_page_len.astype(np.int64), 0)
+            keys += int(lens.sum())
+            pages += int(n.sum())
+        pair_count = int(np.sum(w.kv_lens * qol))  # every branch attends prefix + suffix
+    else:
+        keys = int(w.kv_lens.sum())
+        pages = int(np.diff(w.kv_indptr.astype(np.int64)).sum())
+        if w.causal:
+            prefix = w.kv_lens - qol
+            pair_count = int(np.sum(qol * prefix + qol * (qol + 1) // 2))
+        else:
+            pair_count = int(np.sum(w.kv_lens * qol))
+    kv_bytes = 2 * keys * h_kv * d * elt
+    qo_bytes = 2 * total_qo * h_qo * d * elt + total_qo * h_qo * 4
+    idx_bytes = 4 * pages
+    flops = 4 * d * h_qo * pair_count
+    return dict(bytes=kv_bytes + qo_bytes + idx_bytes, kv_bytes=kv_bytes, flops=flops)
+
+
+def timed_steps(fn, steps, warmup, stream, flush):
+    """Per-step HIP-event times (ms) of fn(), each preceded by a cache flush."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush.add_(1)
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]), wall
+
+
+def bench_workload(name, steps, warmup, flush, graph=True):
+    import torch
+
+    from serving_attention_bsr_amd import lib
+    from serving_attention_bsr_amd import workloads as W
+
+    print(f"[bench] {name}: building inputs", file=sys.stderr, flush=True)
+    w = W.named(name)
+    composable = w.formats is not None
+    dev = torch.device("cuda:0")
+    q, k, v = w.q.to(dev), w.k_pool.to(dev), w.v_pool.to(dev)
+    idx_host = w.kv_indices_formats if composable else w.kv_indices
+    idx = torch.from_numpy(np.ascontiguousarray(idx_host)).to(dev)
+    max_batch = w.batch + (sum(len(f.qo_indptr) - 1 for f in w.formats) if composable else 0)
+    h = lib.BsrAttention(
+        w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, dtype=w.dtype, causal=w.causal,
+        logits_soft_cap=w.cap, max_batch=max_batch, max_total_qo=int(w.qo_indptr[-1]),
+        max_total_kv=int(w.kv_lens.sum()), device=0,
+    )
+    work = algorithmic_work(w, composable)
+    out = dict(workload=name, dtype=w.dtype, bytes=work["bytes"], flops=work["flops"])
+    try:
+        t0 = time.perf_counter()
+        reps = 20
+        for _ in range(reps):
+            if composable:
+                info = h.plan_composable([f.as_dict() for f in w.formats], w.batch)
+            else:
+                info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+        torch.cuda.synchronize()
+        out["plan_us"] = (time.perf_counter() - t0) / reps * 1e6
+    except lib.BsrError as exc:
+        out["error"] = str(exc)
+        return out, None
+    out["plan"] = info
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        h.run(q, k, v, idx, o, lse)
+
+    times, wall = timed_steps(step, steps, warmup, stream, flush)
+    h.check()
+    med = float(np.median(times))
+    out["ms_median"] = med
+    out["ms_min"] = float(times.min())
+    out["ms_mean"] = float(times.mean())
+    out["wall_s"] = wall
+    gbs = work["bytes"] / (med * 1e-3) / 1e9
+    tfl = work["flops"] / (med * 1e-3) / 1e12
+    out["hbm_GBps"] = gbs
+    out["hbm_frac"] = gbs / HBM_PEAK_GBS
+    out["tflops"] = tfl
+    out["mfma_frac"] = tfl / BF16_MFMA_PEAK_TFLOPS
+    if graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                step()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step()
+            gt, _ = timed_steps(g.replay, steps, warmup, stream, flush)
+            out["graph_ms_median"] = float(np.median(gt))
+        except Exception as exc:  # report, do not hide
+            out["graph_error"] = repr(exc)
+    return out, (w, h)
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The oracle as it stands, on the full workload, repeated for about budget_s."""
+    import threadpoolctl
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    q = w.q.double().numpy()
+    k = w.k_pool.float().numpy()
+    v = w.v_pool.float().numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    with threadpoolctl.threadpool_limits(limits=cores):
+        while True:
+            oracle.bsr_attention(
+                q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, w.page_size,
+                w.num_qo_heads, w.num_kv_heads, w.scale, w.causal, w.cap,
+            )
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = (time.perf_counter() - t0) / reps
+    work = algorithmic_work(w)
+    return dict(
+        value=work["bytes"] / dt / 1e12,
+        unit="TB/s",
+        cores=cores,
+        kind="oracle",
+        sample=f"whole {w.name} workload ({w.batch} requests, all heads), {reps} repetition(s), {dt:.2f} s each",
+        seconds_per_step=dt,
+    )
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default=",".join(ALL))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda:0") if args.flush_mib > 0 else None
+    names = [n for n in args.workloads.split(",") if n]
+    if HEADLINE not in names:
+        names = [HEADLINE] + names
+    results = {}
+    keep = {}
+    for name in names:
+        r, ctx = bench_workload(name, args.steps, args.warmup, flush, graph=not args.no_graph)
+        results[name] = r
+        print(f"[bench] {name}: {json.dumps({k: v for k, v in r.items() if k != 'plan'})}", file=sys.stderr, flush=True)
+        if name == HEADLINE:
+            keep[name] = ctx
+        else:
+            del ctx
+            torch.cuda.empty_cache()
+    head = results[HEADLINE]
+    if "error" in head:
+        raise RuntimeError(head["error"])
+    ms = head["ms_median"]
+    gbs = head["hbm_GBps"]
+    prof = torch.cuda.get_device_properties(0)
+    line = {
+        "metric": METRIC,
+        "value": round(gbs / 1000.0, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": HEADLINE,
+            "batch": 64,
+            "qo_len": 1,
+            "kv_len": "uniform[512,8192]",
+            "page_size": 16,
+            "heads": "32q/8kv",
+            "head_dim": 128,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "device": {"name": prof.name, "arch": getattr(prof, "gcnArchName", ""), "cus": prof.multi_processor_count},
+        "workloads": {
+            n: {k: v for k, v in r.items() if k not in ("plan",)} | ({"plan": r["plan"]} if "plan" in r else {})
+            for n, r in results.items()
+        },
+    }
+    if not args.no_cpu_baseline:
+        w, _h = keep[HEADLINE]
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

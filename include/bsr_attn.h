@@ -1,0 +1,198 @@
+/*
+ * bsr_attn.h -- C ABI of an MI355X (gfx950) library for attention over a KV cache
+ * stored as a block-sparse-row (BSR) matrix.
+ *
+ * Sources: the FlashInfer explainer page on zenmind.me ("FlashInfer：面向 LLM 推理
+ * 服务的高效可定制注意力引擎", restating the MLSys 2025 paper), cited below by
+ * its section names:
+ *   - Terms "BSR" and Core mechanism 1 (paper section 3.1.1, Figure 2): the KV
+ *     cache is a BSR matrix; block row r of the matrix reads the physical pages
+ *     kv_indices[kv_indptr[r] .. kv_indptr[r+1]); any page size is allowed.
+ *   - Terms "ragged tensor": Q and O of all requests packed without padding and
+ *     addressed by qo_indptr.
+ *   - Terms "Attention State and ⊕" (paper section 2.2): the result of attention is
+ *     the state (O, LSE); partial states of key chunks are combined with ⊕.
+ *   - Terms "plan()/run()" and Core mechanism 6 (paper Algorithm 1, section
+ *     3.3.1, Figure 6): a host planner runs once per generation step from the
+ *     sequence lengths only, balances work over a fixed number of workgroups
+ *     with cost alpha*l_q + beta*l_kv, caps KV chunks at
+ *     L_kv = sum(ceil(l_qo/T_q) * l_kv) / #workgroups, assigns the longest work
+ *     first through a priority queue, and merges partial states without atomic
+ *     aggregation in an order fixed by the lengths.
+ *   - Core mechanism 7 (paper section 3.3.1, Appendix D): the run kernel is
+ *     persistent with a fixed grid; the workspace is sized for the maxima given at
+ *     set-up and its segments sit at constant offsets; the plan is staged in host
+ *     memory and copied asynchronously; only long requests are split, short ones
+ *     write the final output directly; partial outputs are bounded by
+ *     2 * #workgroups * T_q * H_qo * (D + 1) values.
+ *   - Core mechanism 8 (paper Appendix E): the caller may set the number of
+ *     workgroups attention uses.
+ *   - Terms "composable formats" and Core mechanism 2 (paper section 3.1.2,
+ *     Figure 3): the KV matrix may be split into several BSR sub-matrices (for
+ *     example a shared prefix read by many query rows and per-request suffixes);
+ *     only index arrays differ, no KV data moves.
+ *   - Terms "GQA head-group fusion" (paper Appendix A, Figure 11): query head h
+ *     reads KV head h / g with g = H_qo / H_kv; the g heads of a group are folded
+ *     into the query-length dimension of one work item.
+ *
+ * Layouts (all row-major, last index contiguous):
+ *   Q, O           [sum l_qo, H_qo, D]    dtype of the handle (fp32 or bf16)
+ *   LSE            [sum l_qo, H_qo]       fp32, natural logarithm
+ *   K pool, V pool [num_pages, H_kv, P, D] dtype of the handle
+ *   qo_indptr      int32 [B + 1]   query tokens of block row r: [qo_indptr[r], qo_indptr[r+1])
+ *   kv_indptr      int32 [B + 1]   pages of block row r: kv_indices[kv_indptr[r] .. kv_indptr[r+1])
+ *   kv_indices     int32 [nnz]     physical page ids (device memory)
+ *   last_page_len  int32 [B]       valid slots in the last page, 1..P (ignored for empty rows)
+ * Block row r holds l_kv = (n_pages - 1) * P + last_page_len[r] tokens; token tau
+ * is slot tau % P of page kv_indices[kv_indptr[r] + tau / P].
+ *
+ * Semantics: O = softmax(S) V and LSE = log(sum exp(S)) per query row and head,
+ * where S = sm_scale * q.k, then S = cap * tanh(S / cap) when a soft-cap is set,
+ * then, for causal handles, key j of a block row is hidden from its t-th query
+ * token (0-based) when j > l_kv - l_qo + t.  A row that sees no key gives O = 0
+ * and LSE = -inf.
+ *
+ * Ownership: the library allocates no device memory.  The caller allocates the
+ * workspace (device) and the staging buffer (host; page-locked for an
+ * asynchronous upload) with the sizes bsr_attn_workspace_size() reports, and keeps
+ * both alive and unchanged in address while plans and runs use them.  Host arrays
+ * passed to the plan calls are read during the call only.
+ *
+ * Errors: every call returns a bsr_status; on failure nothing is launched and
+ * bsr_attn_last_error() returns a message for the calling thread.  A handle is
+ * not thread-safe.  Streams are hipStream_t passed as void* (NULL = null stream).
+ */
+#ifndef BSR_ATTN_H
+#define BSR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSR_ATTN_ABI_VERSION 1
+
+typedef enum bsr_status {
+  BSR_OK = 0,
+  BSR_ERR_INVALID_ARG = 1, /* malformed arguments or index arrays */
+  BSR_ERR_CAPACITY = 2,    /* a plan exceeds the maxima given at create time */
+  BSR_ERR_UNSUPPORTED = 3, /* shape or option the library does not implement */
+  BSR_ERR_HIP = 4,         /* a HIP runtime call failed */
+  BSR_ERR_DEVICE = 5       /* the device reported an error (see bsr_attn_check) */
+} bsr_status;
+
+typedef enum bsr_dtype { BSR_DTYPE_F32 = 0, BSR_DTYPE_BF16 = 1 } bsr_dtype;
+
+typedef struct bsr_attn_config {
+  int32_t num_qo_heads;    /* H_qo */
+  int32_t num_kv_heads;    /* H_kv; must divide H_qo */
+  int32_t head_dim;        /* D in {64, 128, 256} */
+  int32_t page_size;       /* P >= 1 (Bc of the BSR matrix) */
+  int32_t dtype;           /* bsr_dtype of Q, K, V and O */
+  int32_t causal;          /* 0 or 1; bottom-right aligned mask */
+  float sm_scale;          /* <= 0 selects 1 / sqrt(D) */
+  float logits_soft_cap;   /* 0 disables; otherwise S = cap * tanh(S / cap) */
+  int32_t max_batch;       /* most block rows of one plan (all formats together) */
+  int32_t max_total_qo;    /* most query tokens (rows of Q) of one plan */
+  int64_t max_total_kv;    /* most KV tokens summed over the block rows of one plan */
+  int32_t num_workgroups;  /* persistent grid size; 0 = what the device keeps resident */
+  int32_t cost_alpha;      /* work-item cost weights alpha, beta; 0 selects 1 */
+  int32_t cost_beta;
+  int32_t min_kv_chunk;    /* smallest KV chunk the planner cuts, tokens; 0 selects 64 */
+  int32_t max_partial_rows;/* partial-state capacity in folded rows; 0 = derived bound */
+  int32_t reserved[3];     /* must be 0 */
+} bsr_attn_config;
+
+/* One BSR sub-matrix for bsr_attn_plan_composable().  Arrays are host memory. */
+typedef struct bsr_format {
+  int32_t num_block_rows;
+  const int32_t* qo_indptr;     /* [num_block_rows + 1] query-token ranges into Q/O */
+  const int32_t* kv_indptr;     /* [num_block_rows + 1] page ranges, relative to the offset */
+  const int32_t* last_page_len; /* [num_block_rows] */
+  int32_t kv_indices_offset;    /* first entry of this format inside kv_indices */
+} bsr_format;
+
+typedef struct bsr_plan_info {
+  int32_t kernel;          /* 1 = VALU decode body, 2 = MFMA tile body, 3 = both */
+  int32_t num_workgroups;  /* grid of the kernel this plan runs */
+  int32_t num_items;       /* attention work items */
+  int32_t num_partial_items;
+  int32_t num_partial_rows;
+  int32_t num_merge_tasks;
+  int32_t num_merge_sources;
+  int32_t q_tile;          /* folded query rows per work item (T_q) */
+  int64_t kv_chunk;        /* L_kv: longest KV chunk of a work item, tokens */
+  int64_t max_wg_cost;     /* largest per-workgroup cost after assignment */
+  int64_t total_cost;
+  int32_t blob_bytes;      /* bytes of plan uploaded to the workspace */
+  int32_t reserved;
+} bsr_plan_info;
+
+typedef struct bsr_attn* bsr_attn_t;
+
+/* Create a handle.  device >= 0 selects a HIP device (made current during calls);
+ * device = -1 creates a host-only handle that can plan (into the staging buffer,
+ * nothing uploaded) but not run; it then needs num_workgroups > 0.  The handle
+ * holds host state only. */
+int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out);
+
+/* Workspace (device) and staging (host) bytes a plan/run pair needs, fixed at create. */
+int bsr_attn_workspace_size(bsr_attn_t h, size_t* device_bytes, size_t* host_bytes);
+
+/* Plan one generation step from the lengths (Core mechanism 6): validate the index
+ * arrays, choose the tile and L_kv, cut chunks, assign work longest-first, build
+ * the merge map, write the plan into host_staging and enqueue its copy into
+ * workspace on stream.  Before rewriting host_staging it waits for the previous
+ * copy from it.  Deterministic: the same lengths give the same plan bytes.
+ * Not capturable in a HIP graph.  workspace may be NULL (then nothing is uploaded;
+ * required for host-only handles).  Returns BSR_ERR_CAPACITY beyond the maxima,
+ * BSR_ERR_INVALID_ARG for non-monotone indptrs, last_page_len outside [1, P] for a
+ * non-empty row, or (causal) a row with l_qo > l_kv. */
+int bsr_attn_plan(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                  const int32_t* last_page_len, int32_t batch, void* workspace,
+                  void* host_staging, void* stream);
+
+/* Plan over several BSR sub-matrices of one KV matrix (Core mechanism 2).  A query
+ * token's keys are the union of the keys of the block rows that cover it, in format
+ * order; the formats must not overlap in keys (caller contract).  Causal handles
+ * are not supported here.  Same staging/upload contract as bsr_attn_plan. */
+int bsr_attn_plan_composable(bsr_attn_t h, int32_t num_formats, const bsr_format* formats,
+                             int32_t total_qo, void* workspace, void* host_staging,
+                             void* stream);
+
+/* Statistics of the last plan made on this handle. */
+int bsr_attn_plan_get_info(bsr_attn_t h, bsr_plan_info* info);
+
+/* Run the last plan: one launch of the persistent kernel on stream (asynchronous).
+ * q, k_pool, v_pool, kv_indices, o, lse (nullable) and workspace are device
+ * pointers in the layouts above; kv_indices must be the array the plan's
+ * kv_indptr (and format offsets) index, with page ids < the pool's page count
+ * (caller contract, not checked).  No allocation, no synchronisation, constant
+ * grid: capturable in a HIP graph; a captured run replays any later plan with the
+ * same kernel kind (bsr_plan_info.kernel) and pointers. */
+int bsr_attn_run(bsr_attn_t h, const void* q, const void* k_pool, const void* v_pool,
+                 const int32_t* kv_indices, void* o, float* lse, void* workspace,
+                 void* stream);
+
+/* Synchronise stream and report whether the device flagged an error during the
+ * runs since the last plan (a bounded wait that expired).  BSR_OK if none. */
+int bsr_attn_check(bsr_attn_t h, void* workspace, void* stream);
+
+/* Stand-alone ⊕ of two sets of attention states (Terms "Attention State and ⊕"):
+ * o_a, o_b, o: fp32 [rows, D]; lse_a, lse_b, lse: fp32 [rows] natural log.
+ * (0, -inf) is the identity.  Device pointers; o/lse may alias an input. */
+int bsr_attn_merge_states(const float* o_a, const float* lse_a, const float* o_b,
+                          const float* lse_b, float* o, float* lse, int64_t rows,
+                          int32_t head_dim, void* stream);
+
+void bsr_attn_destroy(bsr_attn_t h);
+const char* bsr_attn_last_error(void);
+int bsr_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSR_ATTN_H */

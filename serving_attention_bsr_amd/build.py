@@ -1,0 +1,74 @@
+"""Build libbsr_attn.so in-tree with hipcc for gfx950.
+
+Every HIP source is compiled with packed-FP32 instruction selection disabled.
+The host-side sources (planner, C ABI) go through hipcc as well, since the ABI
+launches kernels through the HIP runtime.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(HERE, "libbsr_attn.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+ARCH = "gfx950"
+HIP_SOURCES = ["kernels_d64.hip", "kernels_d128.hip", "kernels_d256.hip", "merge_states.hip"]
+HOST_SOURCES = ["api.cpp", "plan.cpp"]
+COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc():
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found")
+    return path
+
+
+def _run(cmd):
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    lines = [l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l]
+    return proc.returncode, "\n".join(lines)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs_list = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        jobs_list.append([hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))
+        jobs_list.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        results = list(ex.map(_run, jobs_list))
+    failed = False
+    for cmd, (rc, out) in zip(jobs_list, results):
+        if verbose or rc != 0:
+            sys.stderr.write(" ".join(cmd) + "\n" + out + "\n")
+        failed |= rc != 0
+    if failed:
+        raise RuntimeError("HIP build failed")
+    objs = [c[-1] for c in jobs_list]
+    tmp = OUT + ".tmp"
+    rc, out = _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    if rc != 0:
+        sys.stderr.write(out + "\n")
+        raise RuntimeError("link failed")
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

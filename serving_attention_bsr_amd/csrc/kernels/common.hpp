@@ -1,0 +1,109 @@
+// common.hpp -- gfx950 device helpers shared by the attention bodies.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../layout.h"
+#include "../params.h"
+
+namespace bsr {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// tanh from its exponential definition: tanh|x| = (1 - e) / (1 + e), e = exp(-2|x|).
+__device__ __forceinline__ float tanh_exp(float x) {
+  const float ax = __builtin_fabsf(x);
+  const float e = fast_exp2(-2.0f * kLog2e * ax);
+  const float t = (1.0f - e) * fast_rcp(1.0f + e);
+  return __builtin_copysignf(t, x);
+}
+
+// Unsigned division of n < 2^31 by a divisor fixed at set-up (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994).
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t magic, int32_t shift) {
+  return (__umulhi(magic, n) + n) >> shift;
+}
+
+// bf16 <-> fp32.  A bf16 is the high half of an fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane moves (row = 16 lanes).  Control words of the gfx9 DPP encoding.
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N in 1, 2, 4, 8, 16); every lane of a group
+// ends with the group's sum.  Quad steps pair lanes by xor; the mirror steps pair
+// each lane with one of the other half, whose value is already the half's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group size");
+  if constexpr (N >= 2) x += dpp_mov<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp_mov<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp_mov<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_mov<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Workspace views.
+__device__ __forceinline__ const PlanHeader* plan_header(const uint8_t* ws) {
+  return reinterpret_cast<const PlanHeader*>(ws);
+}
+__device__ __forceinline__ int32_t* plan_i32(uint8_t* ws, int32_t off) {
+  return reinterpret_cast<int32_t*>(ws + off);
+}
+
+// Publish a ready stamp after this workgroup's partial-state stores: every thread
+// makes its own stores visible device-wide, the workgroup meets, then one thread
+// releases the stamp.
+__device__ __forceinline__ void publish_flag(int32_t* flag, int32_t epoch) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+constexpr int kMaxSpins = 1 << 21;
+
+// Wait (bounded) until *flag == epoch.  Returns false if the bound expired.
+__device__ __forceinline__ bool wait_flag(const int32_t* flag, int32_t epoch) {
+  int spins = 0;
+  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > kMaxSpins) return false;
+  }
+  return true;
+}
+
+}  // namespace bsr

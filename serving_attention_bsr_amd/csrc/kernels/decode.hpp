@@ -1,0 +1,310 @@
+// decode.hpp -- VALU attention body for work items with few folded query rows.
+//
+// Terms "GQA head-group fusion" of the FlashInfer explainer page (paper
+// Appendix A, Figure 11): the g query heads that share a KV head are folded into
+// the query dimension, so one load of a KV row serves the whole group.  Core
+// mechanism 4 (paper section 3.2.2): with a query tile below the matrix-core
+// minimum the body runs on the vector ALUs.  Background (paper section 2.1):
+// decode is memory-bound, so the body is organised around the KV stream.
+//
+// Mapping on a 64-lane wavefront: a KV row of D elements is read by D/16 lanes,
+// each holding 16 elements (two 16-byte loads for bf16, four for fp32), so a
+// wavefront reads 1024/D rows per step.  Each lane keeps the folded query rows
+// for its 16 elements in registers, so every KV byte is loaded once, into the
+// lanes that use it, and serves all ROWS query rows: the page gather lands
+// straight in registers; LDS is used only to combine the four wavefronts at the
+// end of an item.  Each group of D/16 lanes runs its own online softmax over the
+// rows it reads (running max and sum in base 2); groups and wavefronts are
+// combined with ⊕ at the end of the item.
+//
+// Page gather (Core mechanism 1, paper section 3.1.1): key tau of the block row
+// is slot tau % P of page kv_indices[page_begin + tau / P].  Page ids are loaded
+// two steps ahead of the K/V rows, and K/V one step ahead of the arithmetic, so
+// a wavefront always has a full step of KV loads in flight.  Keys past the chunk
+// are clamped to its last key and masked, so no unused slot is ever read.
+#pragma once
+
+#include "common.hpp"
+
+namespace bsr {
+
+template <int D, bool BF16, int ROWS, int TB, bool CAP>
+struct DecodeBody {
+  static constexpr int LPT = D / 16;                 // lanes per KV row
+  static constexpr int NG = 64 / LPT;                // KV rows per wavefront step slot
+  static constexpr int ESZ = BF16 ? 2 : 4;           // element bytes
+  static constexpr int NLD = 16 * ESZ / 16;          // 16-byte loads per row per lane
+  static constexpr int EPL = 16 / ESZ;               // elements per 16-byte load
+  static constexpr int TILE = NG * TB;               // keys per wavefront step
+  static constexpr int LDS_FLOATS = kWaves * ROWS * (D + 2);
+  static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+
+  struct Pids {
+    int32_t page[TB];
+    int32_t slot[TB];
+  };
+  struct Kv {
+    uint4 k[TB][NLD];
+    uint4 v[TB][NLD];
+  };
+
+  // element index of accumulator slot j of lane chunk c
+  static __device__ __forceinline__ int elem(int c, int j) {
+    return (j / EPL) * (LPT * EPL) + c * EPL + (j % EPL);
+  }
+
+  static __device__ __forceinline__ void load_pids(const RunParams& p, const WorkItem& it,
+                                                   int tile, int grp, Pids& out) {
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      int tau = it.kv_begin + tile * TILE + i * NG + grp;
+      tau = min(tau, it.kv_end - 1);
+      const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+      out.slot[i] = tau - static_cast<int32_t>(pl) * p.page_size;
+      out.page[i] = p.kv_indices[it.page_begin + static_cast<int32_t>(pl)];
+    }
+  }
+
+  static __device__ __forceinline__ void load_kv(const RunParams& p, const WorkItem& it, int c,
+                                                 const Pids& ids, Kv& out) {
+    const uint8_t* kb = static_cast<const uint8_t*>(p.k_pool);
+    const uint8_t* vb = static_cast<const uint8_t*>(p.v_pool);
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int64_t row =
+          (static_cast<int64_t>(ids.page[i]) * p.h_kv + it.kv_head) * p.page_size + ids.slot[i];
+      const int64_t off = row * (D * ESZ) + c * 16;
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        out.k[i][j] = *reinterpret_cast<const uint4*>(kb + off + j * (LPT * 16));
+        out.v[i][j] = *reinterpret_cast<const uint4*>(vb + off + j * (LPT * 16));
+      }
+    }
+  }
+
+  struct State {
+    float acc[ROWS][16];
+    float m[ROWS];
+    float l[ROWS];
+  };
+
+  static __device__ __forceinline__ float dot_row(const uint4 (&q)[NLD], const uint4 (&k)[NLD]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      if constexpr (BF16) {
+        s = dot2_bf16(q[j].x, k[j].x, s);
+        s = dot2_bf16(q[j].y, k[j].y, s);
+        s = dot2_bf16(q[j].z, k[j].z, s);
+        s = dot2_bf16(q[j].w, k[j].w, s);
+      } else {
+        s = __builtin_fmaf(__uint_as_float(q[j].x), __uint_as_float(k[j].x), s);
+        s = __builtin_fmaf(__uint_as_float(q[j].y), __uint_as_float(k[j].y), s);
+        s = __builtin_fmaf(__uint_as_float(q[j].z), __uint_as_float(k[j].z), s);
+        s = __builtin_fmaf(__uint_as_float(q[j].w), __uint_as_float(k[j].w), s);
+      }
+    }
+    return s;
+  }
+
+  static __device__ __forceinline__ void unpack_v(const uint4 (&v)[NLD], float (&out)[16]) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if constexpr (BF16) {
+          out[j * 8 + 2 * t] = bf16_lo(w[t]);
+          out[j * 8 + 2 * t + 1] = bf16_hi(w[t]);
+        } else {
+          out[j * 4 + t] = __uint_as_float(w[t]);
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void step(const RunParams& p, const WorkItem& it, int tile,
+                                              int grp, const uint4 (&q)[ROWS][NLD], const Kv& kv,
+                                              State& st) {
+    float s[TB][ROWS];
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) s[i][r] = group_sum<LPT>(dot_row(q[r], kv.k[i]));
+    const int g = p.group;
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int tau = it.kv_begin + tile * TILE + i * NG + grp;
+      const bool in_chunk = tau < it.kv_end;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        float x;
+        if constexpr (CAP) {
+          x = p.cap_log2 * tanh_exp(s[i][r] * p.sm_scale * p.cap_inv);
+        } else {
+          x = s[i][r] * p.scale_log2;
+        }
+        const bool visible = in_chunk && tau <= it.causal_limit + r / g;
+        s[i][r] = visible ? x : kNegInf;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      float mx = s[0][r];
+#pragma unroll
+      for (int i = 1; i < TB; ++i) mx = __builtin_fmaxf(mx, s[i][r]);
+      const float m_new = __builtin_fmaxf(st.m[r], mx);
+      const float m_use = m_new == kNegInf ? 0.0f : m_new;
+      const float alpha = fast_exp2(st.m[r] - m_use);
+      float psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        s[i][r] = fast_exp2(s[i][r] - m_use);
+        psum += s[i][r];
+      }
+      st.l[r] = st.l[r] * alpha + psum;
+      st.m[r] = m_new;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[r][e] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      float v[16];
+      unpack_v(kv.v[i], v);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.acc[r][e] = __builtin_fmaf(s[i][r], v[e], st.acc[r][e]);
+    }
+  }
+
+  // Attention of one work item; result in the workgroup-combined (O, log2-sum-exp)
+  // handed to `emit(row, d_pair, o0, o1, lse2)`.
+  template <typename Emit>
+  static __device__ void run(const RunParams& p, const WorkItem& it, float* lds, Emit&& emit) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane % LPT;
+    const int grp = lane / LPT;
+    const int g = p.group;
+    const int rows_valid = it.qo_count * g;
+
+    // folded query rows: row r = token (r / g) of the tile, head kv_head * g + r % g
+    uint4 q[ROWS][NLD];
+    {
+      const uint8_t* qb = static_cast<const uint8_t*>(p.q);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        if (r < rows_valid) {
+          const int64_t qrow = static_cast<int64_t>(it.qo_begin + r / g) * p.h_qo +
+                               it.kv_head * g + r % g;
+          const uint8_t* src = qb + qrow * (D * ESZ) + c * 16;
+#pragma unroll
+          for (int j = 0; j < NLD; ++j) q[r][j] = *reinterpret_cast<const uint4*>(src + j * (LPT * 16));
+        } else {
+#pragma unroll
+          for (int j = 0; j < NLD; ++j) q[r][j] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+
+    State st;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      st.m[r] = kNegInf;
+      st.l[r] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[r][e] = 0.0f;
+    }
+
+    const int ntok = it.kv_end - it.kv_begin;
+    const int ntiles = (ntok + TILE - 1) / TILE;
+    int t = wave;
+    Pids pa, pb;
+    Kv ka, kb;
+    if (t < ntiles) load_pids(p, it, t, grp, pa);
+    if (t + kWaves < ntiles) load_pids(p, it, t + kWaves, grp, pb);
+    if (t < ntiles) load_kv(p, it, c, pa, ka);
+    while (t < ntiles) {
+      if (t + kWaves < ntiles) load_kv(p, it, c, pb, kb);
+      if (t + 2 * kWaves < ntiles) load_pids(p, it, t + 2 * kWaves, grp, pa);
+      step(p, it, t, grp, q, ka, st);
+      t += kWaves;
+      if (t >= ntiles) break;
+      if (t + kWaves < ntiles) load_kv(p, it, c, pa, ka);
+      if (t + 2 * kWaves < ntiles) load_pids(p, it, t + 2 * kWaves, grp, pb);
+      step(p, it, t, grp, q, kb, st);
+      t += kWaves;
+    }
+
+    // ⊕ across the lane groups of this wavefront (lanes differing in bits >= log2(LPT))
+#pragma unroll
+    for (int mask = LPT; mask < 64; mask <<= 1) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const float mo = shfl_xor_f(st.m[r], mask);
+        const float lo = shfl_xor_f(st.l[r], mask);
+        const float m_new = __builtin_fmaxf(st.m[r], mo);
+        const float m_use = m_new == kNegInf ? 0.0f : m_new;
+        const float a_self = fast_exp2(st.m[r] - m_use);
+        const float a_other = fast_exp2(mo - m_use);
+        st.l[r] = st.l[r] * a_self + lo * a_other;
+        st.m[r] = m_new;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float ao = shfl_xor_f(st.acc[r][e], mask);
+          st.acc[r][e] = st.acc[r][e] * a_self + ao * a_other;
+        }
+      }
+    }
+
+    // ⊕ across the four wavefronts through LDS: [wave][row][D] accumulators then
+    // [wave][row] (m, l)
+    float* lacc = lds;
+    float* lml = lds + kWaves * ROWS * D;
+    if (grp == 0) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) lacc[(wave * ROWS + r) * D + elem(c, e)] = st.acc[r][e];
+      if (c == 0) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          lml[(wave * ROWS + r) * 2] = st.m[r];
+          lml[(wave * ROWS + r) * 2 + 1] = st.l[r];
+        }
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROWS * (D / 2); idx += kWgThreads) {
+      const int r = idx / (D / 2);
+      const int d = (idx % (D / 2)) * 2;
+      if (r >= rows_valid) continue;
+      float mw[kWaves];
+      float big = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        mw[w] = lml[(w * ROWS + r) * 2];
+        big = __builtin_fmaxf(big, mw[w]);
+      }
+      const float m_use = big == kNegInf ? 0.0f : big;
+      float lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float a = fast_exp2(mw[w] - m_use);
+        lsum += lml[(w * ROWS + r) * 2 + 1] * a;
+        o0 += lacc[(w * ROWS + r) * D + d] * a;
+        o1 += lacc[(w * ROWS + r) * D + d + 1] * a;
+      }
+      if (lsum > 0.0f) {
+        const float inv = 1.0f / lsum;
+        emit(r, d, o0 * inv, o1 * inv, big + fast_log2(lsum));
+      } else {
+        emit(r, d, 0.0f, 0.0f, kNegInf);
+      }
+    }
+    __syncthreads();
+  }
+};
+
+}  // namespace bsr

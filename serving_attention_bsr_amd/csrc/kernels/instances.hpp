@@ -1,0 +1,33 @@
+// instances.hpp -- explicit instances of the persistent kernel for one head_dim.
+#pragma once
+
+#include "persistent.hpp"
+#include "registry.h"
+
+namespace bsr {
+
+// KV rows per lane group per wavefront step: two for bf16; one for fp32, whose
+// rows take twice the registers.
+template <bool BF16>
+constexpr int kDecodeTb = BF16 ? 2 : 1;
+
+template <int D, bool BF16, int ROWS, bool CAP>
+inline void add_decode(std::vector<KernelEntry>* out) {
+  out->push_back({KernelKey{kKindDecode, BF16, D, ROWS, CAP},
+                  reinterpret_cast<const void*>(
+                      &bsr_persistent_kernel<D, BF16, ROWS, kDecodeTb<BF16>, CAP, kKindDecode>)});
+}
+
+template <int D>
+inline void register_head_dim(std::vector<KernelEntry>* out) {
+  add_decode<D, true, 4, false>(out);
+  add_decode<D, true, 4, true>(out);
+  add_decode<D, true, 8, false>(out);
+  add_decode<D, true, 8, true>(out);
+  add_decode<D, false, 4, false>(out);
+  add_decode<D, false, 4, true>(out);
+  add_decode<D, false, 8, false>(out);
+  add_decode<D, false, 8, true>(out);
+}
+
+}  // namespace bsr

@@ -1,0 +1,20 @@
+// registry.h -- the persistent-kernel instances built into the library.
+#pragma once
+
+#include <vector>
+
+#include "../params.h"
+
+namespace bsr {
+
+struct KernelEntry {
+  KernelKey key;
+  const void* fn;  // host stub of __global__ void(RunParams)
+};
+
+// Each instance file appends its kernels.
+void register_d64(std::vector<KernelEntry>* out);
+void register_d128(std::vector<KernelEntry>* out);
+void register_d256(std::vector<KernelEntry>* out);
+
+}  // namespace bsr

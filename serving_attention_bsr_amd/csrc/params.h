@@ -1,0 +1,42 @@
+// params.h -- launch arguments of the persistent kernel (host and device).
+#pragma once
+
+#include <stdint.h>
+
+namespace bsr {
+
+// Pointers and handle constants only, so one captured launch replays any later
+// plan of the same kernel.
+struct RunParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* kv_indices;
+  void* o;
+  float* lse;        // may be null
+  uint8_t* ws;       // workspace base: plan blob at offset 0
+  int64_t partial_o_off;
+  int64_t partial_lse_off;
+  int32_t h_qo, h_kv, group, page_size;
+  uint32_t page_magic;  // division by page_size: q = (mulhi(magic, n) + n) >> shift
+  int32_t page_shift;
+  float scale_log2;     // sm_scale * log2(e), used when there is no soft-cap
+  float sm_scale;
+  float cap;            // soft-cap (0: off)
+  float cap_inv;
+  float cap_log2;       // cap * log2(e)
+  int32_t pad;
+};
+
+struct KernelKey {
+  int kind;  // KernelKind
+  bool bf16;
+  int head_dim;
+  int rows;  // decode-body folded rows (0 when the kernel has no decode body)
+  bool cap;
+};
+
+// Host stub of the matching persistent kernel, or null if not built.
+const void* find_kernel(const KernelKey& key);
+
+}  // namespace bsr

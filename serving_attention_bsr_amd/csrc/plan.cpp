@@ -1,0 +1,360 @@
+// plan.cpp -- deterministic host planner.
+//
+// Follows Core mechanism 6 of the FlashInfer explainer page (paper Algorithm 1,
+// section 3.3.1, Figure 6), the query-tile rule of Core mechanism 4 (paper
+// section 3.2.2), and the direct-write rule of Core mechanism 7 (paper
+// Appendix D.2):
+//   1. pick the query tile: the decode body when every block row folds into at
+//      most 8 rows (GQA heads folded into the query dimension), otherwise the
+//      smallest MFMA tile that is at least the mean folded query length;
+//   2. one work unit per (block row, KV head, query tile), with the KV length it
+//      actually reads (causally clipped);
+//   3. L_kv = ceil(sum of unit KV lengths / #workgroups), rounded up to the KV
+//      granule and at least the minimum chunk;
+//   4. units longer than L_kv are cut into equal chunks of at most L_kv; only
+//      those write partial states, the rest write O/LSE directly;
+//   5. cost = alpha * rows + beta * KV tokens; items sorted by cost, longest
+//      first, each given to the least-loaded workgroup (min-heap on
+//      (load, workgroup id)), so the plan depends on the lengths only;
+//   6. partial states get fixed slots; every query token whose result is split
+//      gets a merge task listing its partial states in KV order (format order
+//      first for composed formats), and merge tasks are spread the same way.
+// Ties are broken by creation order, so equal lengths give identical bytes.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstring>
+#include <functional>
+#include <queue>
+#include <utility>
+
+#include "bsr_attn.h"
+
+namespace bsr {
+
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline int32_t align16(int64_t x) { return static_cast<int32_t>(round_up(x, 16)); }
+
+struct Unit {
+  int32_t row;
+  int32_t head;
+  int32_t t0, nt;
+  int32_t l_eff;
+  int32_t causal_limit;
+  bool mfma;
+};
+
+struct Item {
+  WorkItem w;
+  int64_t cost;
+  int32_t unit;
+  int32_t nchunks;
+};
+
+// Least-loaded assignment; returns the workgroup of each entry (indexed like costs).
+void assign_longest_first(const std::vector<int64_t>& costs, std::vector<int64_t>* load,
+                          std::vector<int32_t>* owner, std::vector<int32_t>* order) {
+  const int32_t n = static_cast<int32_t>(costs.size());
+  order->resize(n);
+  for (int32_t i = 0; i < n; ++i) (*order)[i] = i;
+  std::stable_sort(order->begin(), order->end(),
+                   [&](int32_t a, int32_t b) { return costs[a] > costs[b]; });
+  using Slot = std::pair<int64_t, int32_t>;  // (load, workgroup)
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  for (int32_t w = 0; w < static_cast<int32_t>(load->size()); ++w) heap.push({(*load)[w], w});
+  owner->assign(n, -1);
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t i = (*order)[k];
+    Slot s = heap.top();
+    heap.pop();
+    (*owner)[i] = s.second;
+    s.first += costs[i];
+    (*load)[s.second] = s.first;
+    heap.push(s);
+  }
+}
+
+}  // namespace
+
+int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t total_qo,
+              bool composable, PlanResult* out, std::string* err) {
+  const int32_t g = cfg.group;
+  const int32_t h_kv = cfg.h_kv;
+
+  // ---- 1. kernel kind and query tile -----------------------------------------
+  bool any_decode = false, any_wide = false;
+  int64_t max_decode_rows = 0, wide_rows_sum = 0, wide_count = 0;
+  for (const BlockRow& r : rows) {
+    if (r.qo_len == 0) continue;
+    const int64_t fr = static_cast<int64_t>(r.qo_len) * g;
+    if (fr <= kMaxDecodeRows) {
+      any_decode = true;
+      max_decode_rows = std::max(max_decode_rows, fr);
+    } else {
+      any_wide = true;
+      wide_rows_sum += fr;
+      wide_count += 1;
+    }
+  }
+  int32_t kernel = kKindDecode;
+  int32_t decode_rows = max_decode_rows <= 4 ? 4 : 8;
+  int32_t q_tile = decode_rows;
+  if (any_wide) {
+    if (!cfg.bf16) {
+      // fp32 has no MFMA body here: long query rows run as tiles of 8 folded rows
+      if (g > kMaxDecodeRows) {
+        *err = "fp32 with more than 8 query heads per KV head is not supported";
+        return BSR_ERR_UNSUPPORTED;
+      }
+      kernel = kKindDecode;
+      decode_rows = kMaxDecodeRows;
+      q_tile = decode_rows;
+    } else {
+      kernel = any_decode ? kKindMixed : kKindMfma;
+      const int64_t mean = ceil_div(wide_rows_sum, wide_count);
+      int32_t tile = kMfmaTiles[sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]) - 1];
+      for (int32_t t : kMfmaTiles) {
+        if (t >= mean) {
+          tile = t;
+          break;
+        }
+      }
+      if (g > tile) {
+        *err = "query heads per KV head exceed the MFMA tile height";
+        return BSR_ERR_UNSUPPORTED;
+      }
+      q_tile = tile;
+    }
+  }
+  const int32_t nwg = cfg.num_wg[kernel];
+  if (nwg <= 0) {
+    *err = "no workgroup count for the selected kernel";
+    return BSR_ERR_INVALID_ARG;
+  }
+
+  // ---- 2. work units ---------------------------------------------------------
+  std::vector<Unit> units;
+  for (int32_t ri = 0; ri < static_cast<int32_t>(rows.size()); ++ri) {
+    const BlockRow& r = rows[ri];
+    if (r.qo_len == 0) continue;
+    const bool wide = static_cast<int64_t>(r.qo_len) * g > kMaxDecodeRows;
+    const bool mfma = cfg.bf16 && (kernel == kKindMfma || (kernel == kKindMixed && wide));
+    const int32_t tile_tokens = (mfma ? q_tile : decode_rows) / g;
+    for (int32_t h = 0; h < h_kv; ++h) {
+      for (int32_t t0 = 0; t0 < r.qo_len; t0 += tile_tokens) {
+        Unit u;
+        u.row = ri;
+        u.head = h;
+        u.t0 = t0;
+        u.nt = std::min(tile_tokens, r.qo_len - t0);
+        u.mfma = mfma;
+        if (cfg.causal) {
+          u.causal_limit = r.kv_len - r.qo_len + t0;
+          u.l_eff = std::min<int32_t>(r.kv_len, u.causal_limit + u.nt);
+        } else {
+          u.causal_limit = kNoCausal;
+          u.l_eff = r.kv_len;
+        }
+        units.push_back(u);
+      }
+    }
+  }
+
+  // ---- 3. maximum KV chunk ---------------------------------------------------
+  int64_t total_kv = 0;
+  for (const Unit& u : units) total_kv += u.l_eff;
+  int64_t chunk = round_up(std::max<int64_t>(ceil_div(total_kv, nwg), 1), kChunkGranule);
+  chunk = std::max<int64_t>(chunk, round_up(std::max(cfg.min_chunk, 1), kChunkGranule));
+
+  // ---- 4. chunks -> items ----------------------------------------------------
+  std::vector<Item> items;
+  items.reserve(units.size() + 2 * nwg);
+  for (int32_t ui = 0; ui < static_cast<int32_t>(units.size()); ++ui) {
+    const Unit& u = units[ui];
+    const BlockRow& r = rows[u.row];
+    WorkItem w;
+    std::memset(&w, 0, sizeof(w));
+    w.flags = u.mfma ? kItemMfma : 0;
+    w.qo_begin = r.qo_begin + u.t0;
+    w.qo_count = u.nt;
+    w.kv_head = u.head;
+    w.page_begin = r.page_begin;
+    w.causal_limit = u.causal_limit;
+    w.partial_row = -1;
+    w.flag_id = -1;
+    const int64_t frows = static_cast<int64_t>(u.nt) * g;
+    if (u.l_eff == 0) {
+      if (composable) continue;  // contributes no keys to the composed result
+      w.kv_begin = 0;
+      w.kv_end = 0;
+      items.push_back({w, cfg.alpha * frows, ui, 1});
+      continue;
+    }
+    const int64_t n = ceil_div(u.l_eff, chunk);
+    const int64_t csz = n == 1 ? u.l_eff : round_up(ceil_div(u.l_eff, n), kChunkGranule);
+    int32_t made = 0;
+    for (int64_t b = 0; b < u.l_eff; b += csz) {
+      w.kv_begin = static_cast<int32_t>(b);
+      w.kv_end = static_cast<int32_t>(std::min<int64_t>(b + csz, u.l_eff));
+      items.push_back({w, cfg.alpha * frows + cfg.beta * (w.kv_end - w.kv_begin), ui, 0});
+      ++made;
+    }
+    for (int32_t k = 0; k < made; ++k) items[items.size() - 1 - k].nchunks = made;
+  }
+
+  // ---- 5. direct write versus partial ----------------------------------------
+  // (token, head) coverage counts; an item writes O/LSE directly when its unit is
+  // not split and it is the only contributor for every token it covers.
+  std::vector<int32_t> cover(static_cast<size_t>(total_qo) * h_kv, 0);
+  for (const Item& it : items)
+    for (int32_t t = 0; t < it.w.qo_count; ++t)
+      cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] += 1;
+  int64_t partial_rows = 0;
+  int32_t num_flags = 0, num_partial_items = 0;
+  for (Item& it : items) {
+    bool direct = it.nchunks == 1;
+    for (int32_t t = 0; direct && t < it.w.qo_count; ++t)
+      direct = cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] == 1;
+    if (!direct) {
+      it.w.flags |= kItemPartial;
+      it.w.partial_row = static_cast<int32_t>(partial_rows);
+      it.w.flag_id = num_flags++;
+      partial_rows += static_cast<int64_t>(it.w.qo_count) * g;
+      ++num_partial_items;
+    }
+  }
+  if (partial_rows > cfg.max_partial_rows) {
+    *err = "plan needs " + std::to_string(partial_rows) + " partial rows, capacity is " +
+           std::to_string(cfg.max_partial_rows);
+    return BSR_ERR_CAPACITY;
+  }
+
+  // ---- 6. merge map ----------------------------------------------------------
+  // A (token, head) needs a merge task unless a direct item wrote it.
+  std::vector<std::vector<MergeSrc>> srcs_of(static_cast<size_t>(total_qo) * h_kv);
+  std::vector<char> written(static_cast<size_t>(total_qo) * h_kv, 0);
+  std::vector<char> needed(static_cast<size_t>(total_qo) * h_kv, 0);
+  for (const Item& it : items) {
+    for (int32_t t = 0; t < it.w.qo_count; ++t) {
+      const size_t key = static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head;
+      if (it.w.flags & kItemPartial)
+        srcs_of[key].push_back({it.w.partial_row + t * g, it.w.flag_id});
+      else
+        written[key] = 1;
+    }
+  }
+  if (composable) {
+    // tokens a format lists must end up with a result even if no key covers them
+    for (const BlockRow& r : rows)
+      for (int32_t t = 0; t < r.qo_len; ++t)
+        for (int32_t h = 0; h < h_kv; ++h) needed[static_cast<size_t>(r.qo_begin + t) * h_kv + h] = 1;
+  }
+  std::vector<MergeTask> tasks;
+  std::vector<MergeSrc> srcs;
+  for (size_t key = 0; key < srcs_of.size(); ++key) {
+    if (written[key]) continue;
+    if (srcs_of[key].empty() && !needed[key]) continue;
+    MergeTask m;
+    m.qo_row = static_cast<int32_t>(key / h_kv);
+    m.kv_head = static_cast<int32_t>(key % h_kv);
+    m.src_begin = static_cast<int32_t>(srcs.size());
+    m.src_count = static_cast<int32_t>(srcs_of[key].size());
+    srcs.insert(srcs.end(), srcs_of[key].begin(), srcs_of[key].end());
+    tasks.push_back(m);
+  }
+
+  // ---- 7. longest-first assignment -------------------------------------------
+  std::vector<int64_t> load(nwg, 0);
+  std::vector<int64_t> costs(items.size());
+  for (size_t i = 0; i < items.size(); ++i) costs[i] = items[i].cost;
+  std::vector<int32_t> owner, order;
+  assign_longest_first(costs, &load, &owner, &order);
+  std::vector<int64_t> mcosts(tasks.size());
+  for (size_t i = 0; i < tasks.size(); ++i)
+    mcosts[i] = cfg.alpha + cfg.beta * static_cast<int64_t>(tasks[i].src_count) * g;
+  std::vector<int32_t> mowner, morder;
+  assign_longest_first(mcosts, &load, &mowner, &morder);
+  int64_t max_load = 0, total_cost = 0;
+  for (int64_t l : load) {
+    max_load = std::max(max_load, l);
+    total_cost += l;
+  }
+
+  // ---- 8. blob ---------------------------------------------------------------
+  PlanHeader hdr;
+  std::memset(&hdr, 0, sizeof(hdr));
+  hdr.magic = kPlanMagic;
+  hdr.kernel = kernel;
+  hdr.num_wg = nwg;
+  hdr.num_items = static_cast<int32_t>(items.size());
+  hdr.num_merge = static_cast<int32_t>(tasks.size());
+  hdr.num_srcs = static_cast<int32_t>(srcs.size());
+  hdr.num_flags = num_flags;
+  int64_t off = sizeof(PlanHeader);
+  hdr.off_status = align16(off);
+  off = hdr.off_status + 16;
+  hdr.off_epochs = align16(off);
+  off = hdr.off_epochs + 4LL * nwg;
+  hdr.off_flags = align16(off);
+  off = hdr.off_flags + 4LL * num_flags;
+  hdr.off_item_ptr = align16(off);
+  off = hdr.off_item_ptr + 4LL * (nwg + 1);
+  hdr.off_items = align16(off);
+  off = hdr.off_items + static_cast<int64_t>(sizeof(WorkItem)) * items.size();
+  hdr.off_merge_ptr = align16(off);
+  off = hdr.off_merge_ptr + 4LL * (nwg + 1);
+  hdr.off_merge = align16(off);
+  off = hdr.off_merge + static_cast<int64_t>(sizeof(MergeTask)) * tasks.size();
+  hdr.off_srcs = align16(off);
+  off = hdr.off_srcs + static_cast<int64_t>(sizeof(MergeSrc)) * srcs.size();
+  const int64_t bytes = align16(off);
+  if (bytes > cfg.blob_capacity) {
+    *err = "plan of " + std::to_string(bytes) + " bytes exceeds the plan segment (" +
+           std::to_string(cfg.blob_capacity) + " bytes); raise the maxima at create";
+    return BSR_ERR_CAPACITY;
+  }
+  hdr.blob_bytes = static_cast<int32_t>(bytes);
+
+  out->blob.assign(bytes, 0);
+  uint8_t* base = out->blob.data();
+  std::memcpy(base, &hdr, sizeof(hdr));
+  // work queues: items of workgroup w in the order they were assigned
+  {
+    std::vector<int32_t> count(nwg + 1, 0);
+    for (size_t i = 0; i < items.size(); ++i) count[owner[i] + 1] += 1;
+    for (int32_t w = 0; w < nwg; ++w) count[w + 1] += count[w];
+    std::memcpy(base + hdr.off_item_ptr, count.data(), 4 * (nwg + 1));
+    std::vector<int32_t> fill(count.begin(), count.end() - 1);
+    WorkItem* dst = reinterpret_cast<WorkItem*>(base + hdr.off_items);
+    for (int32_t i : order) dst[fill[owner[i]]++] = items[i].w;
+  }
+  {
+    std::vector<int32_t> count(nwg + 1, 0);
+    for (size_t i = 0; i < tasks.size(); ++i) count[mowner[i] + 1] += 1;
+    for (int32_t w = 0; w < nwg; ++w) count[w + 1] += count[w];
+    std::memcpy(base + hdr.off_merge_ptr, count.data(), 4 * (nwg + 1));
+    std::vector<int32_t> fill(count.begin(), count.end() - 1);
+    MergeTask* dst = reinterpret_cast<MergeTask*>(base + hdr.off_merge);
+    for (int32_t i : morder) dst[fill[mowner[i]]++] = tasks[i];
+    if (!srcs.empty()) std::memcpy(base + hdr.off_srcs, srcs.data(), sizeof(MergeSrc) * srcs.size());
+  }
+
+  out->kernel = kernel;
+  out->num_wg = nwg;
+  out->q_tile = q_tile;
+  out->decode_rows = decode_rows;
+  out->num_items = hdr.num_items;
+  out->num_partial_items = num_partial_items;
+  out->num_partial_rows = partial_rows;
+  out->num_merge = hdr.num_merge;
+  out->num_srcs = hdr.num_srcs;
+  out->kv_chunk = chunk;
+  out->max_wg_cost = max_load;
+  out->total_cost = total_cost;
+  return BSR_OK;
+}
+
+}  // namespace bsr

@@ -1,0 +1,59 @@
+// plan.h -- host planner: from sequence lengths to a work queue and merge map.
+//
+// Core mechanism 6 of the FlashInfer explainer page (paper Algorithm 1, section
+// 3.3.1, Figure 6) and the tile heuristic of Core mechanism 4 (paper section
+// 3.2.2).  Pure host C++: no HIP calls, so it is exercised on machines without a
+// GPU through a host-only handle.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "layout.h"
+
+namespace bsr {
+
+struct PlanConfig {
+  int32_t h_qo = 0, h_kv = 0, group = 0, head_dim = 0, page_size = 0;
+  bool causal = false;
+  bool bf16 = false;
+  int32_t num_wg[4] = {0, 0, 0, 0};  // grid per KernelKind (index 1..3)
+  int64_t alpha = 1, beta = 1;
+  int32_t min_chunk = 64;
+  // capacities (plan rejected beyond them)
+  int32_t max_batch = 0, max_total_qo = 0;
+  int64_t max_total_kv = 0;
+  int64_t max_partial_rows = 0;
+  int64_t blob_capacity = 0;
+};
+
+// One block row of one format.
+struct BlockRow {
+  int32_t qo_begin = 0, qo_len = 0;
+  int32_t page_begin = 0;  // absolute index into kv_indices
+  int32_t kv_len = 0;
+  int32_t format = 0;
+};
+
+struct PlanResult {
+  std::vector<uint8_t> blob;  // the bytes to upload
+  int32_t kernel = 0, num_wg = 0, q_tile = 0, decode_rows = 0;
+  int32_t num_items = 0, num_partial_items = 0, num_merge = 0, num_srcs = 0;
+  int64_t num_partial_rows = 0;
+  int64_t kv_chunk = 0, max_wg_cost = 0, total_cost = 0;
+};
+
+// Decode body handles up to this many folded rows per item.
+constexpr int kMaxDecodeRows = 8;
+// KV granularity that chunk lengths are rounded to (tokens).
+constexpr int kChunkGranule = 64;
+// MFMA tile heights (folded rows) the kernels implement, smallest first.
+constexpr int kMfmaTiles[] = {128};
+
+// Returns 0 and fills out, or a bsr_status code with a message in err.
+int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t total_qo,
+              bool composable, PlanResult* out, std::string* err);
+
+}  // namespace bsr

@@ -1,0 +1,362 @@
+"""ctypes binding of libbsr_attn.so (argument marshalling only).
+
+The functions below carry the names of the C entry points declared in
+include/bsr_attn.h and pass raw pointers through; every step of the attention
+runs in the library's HIP kernels.  PyTorch provides device memory (workspace,
+outputs) and the current stream.  If the library is missing the import fails:
+there is no other implementation to fall back to.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsr_attn.so")
+
+BSR_OK = 0
+BSR_ERR_INVALID_ARG = 1
+BSR_ERR_CAPACITY = 2
+BSR_ERR_UNSUPPORTED = 3
+BSR_ERR_HIP = 4
+BSR_ERR_DEVICE = 5
+BSR_DTYPE_F32 = 0
+BSR_DTYPE_BF16 = 1
+
+KERNEL_DECODE = 1
+KERNEL_MFMA = 2
+KERNEL_MIXED = 3
+
+EXPORTED = [
+    "bsr_attn_abi_version",
+    "bsr_attn_last_error",
+    "bsr_attn_create",
+    "bsr_attn_workspace_size",
+    "bsr_attn_plan",
+    "bsr_attn_plan_composable",
+    "bsr_attn_plan_get_info",
+    "bsr_attn_run",
+    "bsr_attn_check",
+    "bsr_attn_merge_states",
+    "bsr_attn_destroy",
+]
+
+
+class BsrError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"bsr_attn error {code}: {msg}")
+        self.code = code
+
+
+class bsr_attn_config(ctypes.Structure):
+    _fields_ = [
+        ("num_qo_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("logits_soft_cap", ctypes.c_float),
+        ("max_batch", ctypes.c_int32),
+        ("max_total_qo", ctypes.c_int32),
+        ("max_total_kv", ctypes.c_int64),
+        ("num_workgroups", ctypes.c_int32),
+        ("cost_alpha", ctypes.c_int32),
+        ("cost_beta", ctypes.c_int32),
+        ("min_kv_chunk", ctypes.c_int32),
+        ("max_partial_rows", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
+    ]
+
+
+class bsr_format(ctypes.Structure):
+    _fields_ = [
+        ("num_block_rows", ctypes.c_int32),
+        ("qo_indptr", ctypes.POINTER(ctypes.c_int32)),
+        ("kv_indptr", ctypes.POINTER(ctypes.c_int32)),
+        ("last_page_len", ctypes.POINTER(ctypes.c_int32)),
+        ("kv_indices_offset", ctypes.c_int32),
+    ]
+
+
+class bsr_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("num_workgroups", ctypes.c_int32),
+        ("num_items", ctypes.c_int32),
+        ("num_partial_items", ctypes.c_int32),
+        ("num_partial_rows", ctypes.c_int32),
+        ("num_merge_tasks", ctypes.c_int32),
+        ("num_merge_sources", ctypes.c_int32),
+        ("q_tile", ctypes.c_int32),
+        ("kv_chunk", ctypes.c_int64),
+        ("max_wg_cost", ctypes.c_int64),
+        ("total_cost", ctypes.c_int64),
+        ("blob_bytes", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+_lib = None
+
+
+def load():
+    """Load libbsr_attn.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_i32, c_i64, vp = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    f32p = ctypes.c_void_p
+    lib.bsr_attn_abi_version.restype = c_int
+    lib.bsr_attn_last_error.restype = ctypes.c_char_p
+    lib.bsr_attn_create.argtypes = [ctypes.POINTER(bsr_attn_config), c_int, ctypes.POINTER(vp)]
+    lib.bsr_attn_workspace_size.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    lib.bsr_attn_plan.argtypes = [vp, i32p, i32p, i32p, c_i32, vp, vp, vp]
+    lib.bsr_attn_plan_composable.argtypes = [vp, c_i32, ctypes.POINTER(bsr_format), c_i32, vp, vp, vp]
+    lib.bsr_attn_plan_get_info.argtypes = [vp, ctypes.POINTER(bsr_plan_info)]
+    lib.bsr_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, f32p, vp, vp]
+    lib.bsr_attn_check.argtypes = [vp, vp, vp]
+    lib.bsr_attn_merge_states.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p, c_i64, c_i32, vp]
+    lib.bsr_attn_destroy.argtypes = [vp]
+    lib.bsr_attn_destroy.restype = None
+    for name in EXPORTED:
+        if name not in ("bsr_attn_last_error", "bsr_attn_destroy"):
+            getattr(lib, name).restype = c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != BSR_OK:
+        raise BsrError(rc, load().bsr_attn_last_error().decode())
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _dptr(t):
+    """Device (or host) address of a torch tensor, None stays None."""
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        return None
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# --------------------------------------------------------------------------- #
+# Entry points under their C names
+# --------------------------------------------------------------------------- #
+
+def bsr_attn_abi_version():
+    return load().bsr_attn_abi_version()
+
+
+def bsr_attn_create(cfg: bsr_attn_config, device: int):
+    h = ctypes.c_void_p()
+    _check(load().bsr_attn_create(ctypes.byref(cfg), device, ctypes.byref(h)))
+    return h
+
+
+def bsr_attn_workspace_size(h):
+    dev, host = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().bsr_attn_workspace_size(h, ctypes.byref(dev), ctypes.byref(host)))
+    return dev.value, host.value
+
+
+def bsr_attn_plan(h, qo_indptr, kv_indptr, last_page_len, workspace, host_staging, stream):
+    qo, kv, last = _i32(qo_indptr), _i32(kv_indptr), _i32(last_page_len)
+    batch = len(qo) - 1
+    _check(load().bsr_attn_plan(h, _ptr(qo), _ptr(kv), _ptr(last), batch, workspace, host_staging, stream))
+
+
+def bsr_attn_plan_composable(h, formats: Sequence[dict], total_qo, workspace, host_staging, stream):
+    keep = []
+    arr = (bsr_format * len(formats))()
+    for i, f in enumerate(formats):
+        qo, kv, last = _i32(f["qo_indptr"]), _i32(f["kv_indptr"]), _i32(f["last_page_len"])
+        keep += [qo, kv, last]
+        arr[i].num_block_rows = len(qo) - 1
+        arr[i].qo_indptr = _ptr(qo)
+        arr[i].kv_indptr = _ptr(kv)
+        arr[i].last_page_len = _ptr(last)
+        arr[i].kv_indices_offset = int(f["kv_indices_offset"])
+    _check(load().bsr_attn_plan_composable(h, len(formats), arr, int(total_qo), workspace, host_staging, stream))
+
+
+def bsr_attn_plan_get_info(h):
+    info = bsr_plan_info()
+    _check(load().bsr_attn_plan_get_info(h, ctypes.byref(info)))
+    return info
+
+
+def bsr_attn_run(h, q, k_pool, v_pool, kv_indices, o, lse, workspace, stream):
+    _check(load().bsr_attn_run(h, q, k_pool, v_pool, kv_indices, o, lse, workspace, stream))
+
+
+def bsr_attn_check(h, workspace, stream):
+    _check(load().bsr_attn_check(h, workspace, stream))
+
+
+def bsr_attn_merge_states(o_a, lse_a, o_b, lse_b, o, lse, rows, head_dim, stream):
+    _check(load().bsr_attn_merge_states(o_a, lse_a, o_b, lse_b, o, lse, rows, head_dim, stream))
+
+
+def bsr_attn_destroy(h):
+    load().bsr_attn_destroy(h)
+
+
+# --------------------------------------------------------------------------- #
+# Convenience wrapper: owns the handle, the workspace and the staging buffer
+# --------------------------------------------------------------------------- #
+
+class BsrAttention:
+    """One handle plus the caller-side buffers the C ABI asks for.
+
+    device >= 0: workspace is a torch uint8 CUDA tensor, staging is pinned host
+    memory.  device = -1: host-only (plans only, into a numpy staging buffer).
+    """
+
+    def __init__(
+        self,
+        num_qo_heads: int,
+        num_kv_heads: int,
+        head_dim: int,
+        page_size: int,
+        dtype: str = "bf16",
+        causal: bool = False,
+        sm_scale: float = 0.0,
+        logits_soft_cap: float = 0.0,
+        max_batch: int = 256,
+        max_total_qo: int = 4096,
+        max_total_kv: int = 1 << 22,
+        num_workgroups: int = 0,
+        device: int = 0,
+        cost_alpha: int = 0,
+        cost_beta: int = 0,
+        min_kv_chunk: int = 0,
+        max_partial_rows: int = 0,
+    ):
+        cfg = bsr_attn_config()
+        cfg.num_qo_heads = num_qo_heads
+        cfg.num_kv_heads = num_kv_heads
+        cfg.head_dim = head_dim
+        cfg.page_size = page_size
+        cfg.dtype = BSR_DTYPE_BF16 if dtype == "bf16" else BSR_DTYPE_F32
+        cfg.causal = int(bool(causal))
+        cfg.sm_scale = sm_scale
+        cfg.logits_soft_cap = logits_soft_cap
+        cfg.max_batch = max_batch
+        cfg.max_total_qo = max_total_qo
+        cfg.max_total_kv = max_total_kv
+        cfg.num_workgroups = num_workgroups
+        cfg.cost_alpha = cost_alpha
+        cfg.cost_beta = cost_beta
+        cfg.min_kv_chunk = min_kv_chunk
+        cfg.max_partial_rows = max_partial_rows
+        self.cfg = cfg
+        self.dtype = dtype
+        self.device = device
+        self.handle = bsr_attn_create(cfg, device)
+        dev_bytes, host_bytes = bsr_attn_workspace_size(self.handle)
+        self.workspace_bytes = dev_bytes
+        if device >= 0:
+            import torch
+
+            self.workspace = torch.zeros(dev_bytes, dtype=torch.uint8, device=f"cuda:{device}")
+            self.staging = torch.empty(host_bytes, dtype=torch.uint8, pin_memory=True)
+            self._ws_ptr = _dptr(self.workspace)
+            self._staging_ptr = _dptr(self.staging)
+        else:
+            self.workspace = None
+            self.staging = np.zeros(host_bytes, dtype=np.uint8)
+            self._ws_ptr = None
+            self._staging_ptr = ctypes.c_void_p(self.staging.ctypes.data)
+
+    def _stream(self):
+        if self.device < 0:
+            return None
+        import torch
+
+        return _stream_ptr(torch.cuda.current_stream(self.device))
+
+    def plan(self, qo_indptr, kv_indptr, last_page_len):
+        bsr_attn_plan(self.handle, qo_indptr, kv_indptr, last_page_len, self._ws_ptr, self._staging_ptr, self._stream())
+        return self.info()
+
+    def plan_composable(self, formats, total_qo):
+        bsr_attn_plan_composable(self.handle, formats, total_qo, self._ws_ptr, self._staging_ptr, self._stream())
+        return self.info()
+
+    def info(self):
+        return bsr_attn_plan_get_info(self.handle).as_dict()
+
+    def plan_bytes(self) -> np.ndarray:
+        """Copy of the last plan as staged on the host."""
+        n = self.info()["blob_bytes"]
+        if self.device >= 0:
+            return self.staging[:n].numpy().copy()
+        return self.staging[:n].copy()
+
+    def run(self, q, k_pool, v_pool, kv_indices, o=None, lse=None):
+        import torch
+
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+        bsr_attn_run(
+            self.handle, _dptr(q), _dptr(k_pool), _dptr(v_pool), _dptr(kv_indices), _dptr(o), _dptr(lse),
+            self._ws_ptr, self._stream(),
+        )
+        return o, lse
+
+    def check(self):
+        bsr_attn_check(self.handle, self._ws_ptr, self._stream())
+
+    def close(self):
+        if self.handle is not None:
+            bsr_attn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def merge_states(o_a, lse_a, o_b, lse_b, o=None, lse=None):
+    """⊕ of two fp32 state arrays on the GPU (o: [rows, D], lse: [rows])."""
+    import torch
+
+    rows, d = o_a.shape
+    if o is None:
+        o = torch.empty_like(o_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    bsr_attn_merge_states(
+        _dptr(o_a), _dptr(lse_a), _dptr(o_b), _dptr(lse_b), _dptr(o), _dptr(lse), rows, d,
+        _stream_ptr(torch.cuda.current_stream(o_a.device)),
+    )
+    return o, lse

@@ -153,8 +153,12 @@ def build(
     pool_pages: Optional[int] = None,
     rng: Optional[np.random.Generator] = None,
     poison: bool = True,
+    tensors: bool = True,
 ) -> Workload:
-    """A single-format workload from explicit lengths (lengths drawn by the caller)."""
+    """A single-format workload from explicit lengths (lengths drawn by the caller).
+
+    tensors=False builds the index arrays only (q, k_pool, v_pool are None).
+    """
     if rng is None:
         rng = np.random.Generator(np.random.PCG64(seed))
     qo_lens = np.asarray(qo_lens, dtype=np.int64)
@@ -166,10 +170,12 @@ def build(
     kv_indptr, kv_indices, last = _page_table(kv_lens, page_size, perm)
     qo_indptr = np.zeros(len(qo_lens) + 1, dtype=np.int64)
     qo_indptr[1:] = np.cumsum(qo_lens)
-    q, k, v = _draw_tensors(
-        seed, int(qo_indptr[-1]), pool_pages, num_qo_heads, num_kv_heads, page_size, head_dim, dtype
-    )
-    if poison:
+    q = k = v = None
+    if tensors:
+        q, k, v = _draw_tensors(
+            seed, int(qo_indptr[-1]), pool_pages, num_qo_heads, num_kv_heads, page_size, head_dim, dtype
+        )
+    if tensors and poison:
         pages, slots = _used_slots(kv_indptr, kv_indices, last, page_size)
         _poison_unused(k, pages, slots)
         _poison_unused(v, pages, slots)
@@ -200,43 +206,45 @@ def build(
 # and parallel generation over a shared prefix).
 # --------------------------------------------------------------------------- #
 
-def tiny_decode_f32(seed=1):
+def tiny_decode_f32(seed=1, tensors=True):
     """4 decode requests, KV {17, 64, 100, 255}, P=16, 64-page pool, 8/2 heads, D=64, fp32."""
     return build(
         "tiny_decode_f32", seed, [1, 1, 1, 1], [17, 64, 100, 255], 16, 8, 2, 64,
-        dtype="f32", pool_pages=64,
+        dtype="f32", pool_pages=64, tensors=tensors,
     )
 
 
-def batch_decode(seed=2, batch=64, lo=512, hi=8192):
+def batch_decode(seed=2, batch=64, lo=512, hi=8192, tensors=True):
     """Batch decode, Llama-3-8B attention shape: 32/8 heads, D=128, P=16, bf16."""
     rng = np.random.Generator(np.random.PCG64(seed))
     kv = rng.integers(lo, hi, size=batch, endpoint=True)
-    return build("batch_decode", seed, [1] * batch, kv, 16, 32, 8, 128, dtype="bf16", rng=rng)
+    return build("batch_decode", seed, [1] * batch, kv, 16, 32, 8, 128, dtype="bf16", rng=rng, tensors=tensors)
 
 
-def skewed_long_decode(seed=3, long_len=131072, short_len=1024, n_short=15, cap=30.0):
+def skewed_long_decode(seed=3, long_len=131072, short_len=1024, n_short=15, cap=30.0, tensors=True):
     """One 131072-token request and 15 of 1024 tokens, soft-cap 30, 32/8 heads, D=128."""
     rng = np.random.Generator(np.random.PCG64(seed))
     kv = [long_len] + [short_len] * n_short
     return build(
-        "skewed_long_decode", seed, [1] * len(kv), kv, 16, 32, 8, 128, dtype="bf16", cap=cap, rng=rng
+        "skewed_long_decode", seed, [1] * len(kv), kv, 16, 32, 8, 128, dtype="bf16", cap=cap, rng=rng,
+        tensors=tensors,
     )
 
 
-def ragged_causal_prefill(seed=4, batch=8, qo_lo=128, qo_hi=4096, pre_lo=0, pre_hi=4096):
+def ragged_causal_prefill(seed=4, batch=8, qo_lo=128, qo_hi=4096, pre_lo=0, pre_hi=4096, tensors=True):
     """Causal prefill: l_qo ~ U[128,4096], cached prefix ~ U[0,4096], P=1, 32/8 heads, D=128."""
     rng = np.random.Generator(np.random.PCG64(seed))
     qo = rng.integers(qo_lo, qo_hi, size=batch, endpoint=True)
     prefix = rng.integers(pre_lo, pre_hi, size=batch, endpoint=True)
     return build(
-        "ragged_causal_prefill", seed, qo, prefix + qo, 1, 32, 8, 128, dtype="bf16", causal=True, rng=rng
+        "ragged_causal_prefill", seed, qo, prefix + qo, 1, 32, 8, 128, dtype="bf16", causal=True, rng=rng,
+        tensors=tensors,
     )
 
 
 def shared_prefix_composable(
     seed=5, branches=64, prefix_len=8192, suf_lo=64, suf_hi=512, page_size=16,
-    num_qo_heads=32, num_kv_heads=8, head_dim=256, dtype="bf16",
+    num_qo_heads=32, num_kv_heads=8, head_dim=256, dtype="bf16", tensors=True,
 ):
     """Parallel generation: `branches` decode rows share one prefix, each with its own suffix.
 
@@ -264,11 +272,13 @@ def shared_prefix_composable(
         single_indptr.append(single_indptr[-1] + n_prefix_pages + int(n_suf_pages[b]))
     single_indices = np.concatenate(single_indices).astype(np.int32)
     qo_indptr = np.arange(branches + 1, dtype=np.int32)
-    q, k, v = _draw_tensors(seed, branches, pool_pages, num_qo_heads, num_kv_heads, page_size, head_dim, dtype)
-    pages = list(prefix_pages) + list(suf_indices)
-    slots = [page_size] * n_prefix_pages + _used_slots(suf_indptr, suf_indices, suf_last, page_size)[1]
-    _poison_unused(k, pages, slots)
-    _poison_unused(v, pages, slots)
+    q = k = v = None
+    if tensors:
+        q, k, v = _draw_tensors(seed, branches, pool_pages, num_qo_heads, num_kv_heads, page_size, head_dim, dtype)
+        pages = list(prefix_pages) + list(suf_indices)
+        slots = [page_size] * n_prefix_pages + _used_slots(suf_indptr, suf_indices, suf_last, page_size)[1]
+        _poison_unused(k, pages, slots)
+        _poison_unused(v, pages, slots)
     formats = [
         Format(
             qo_indptr=np.array([0, branches], dtype=np.int32),

@@ -1,0 +1,60 @@
+"""The C-ABI library loads on a machine without a GPU and exports what the header declares."""
+
+import os
+import re
+
+import pytest
+
+from serving_attention_bsr_amd import lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "bsr_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsr_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    so = lib.load()
+    for name in declared_functions():
+        assert hasattr(so, name), name
+
+
+def test_abi_version():
+    assert lib.bsr_attn_abi_version() == 1
+
+
+def test_struct_sizes_match_header():
+    # bsr_attn_config: 8 int32/float, max_batch, max_total_qo, int64, 5 int32, reserved[3]
+    assert lib.ctypes.sizeof(lib.bsr_attn_config) == 80
+    assert lib.ctypes.sizeof(lib.bsr_plan_info) == 64
+
+
+def test_host_only_handle_needs_workgroups():
+    with pytest.raises(lib.BsrError) as e:
+        lib.BsrAttention(8, 2, 64, 16, dtype="f32", device=-1)
+    assert e.value.code == lib.BSR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize(
+    "kw, code",
+    [
+        (dict(num_qo_heads=6, num_kv_heads=4), lib.BSR_ERR_INVALID_ARG),
+        (dict(head_dim=96), lib.BSR_ERR_UNSUPPORTED),
+        (dict(page_size=0), lib.BSR_ERR_INVALID_ARG),
+        (dict(logits_soft_cap=-1.0), lib.BSR_ERR_INVALID_ARG),
+        (dict(max_batch=0), lib.BSR_ERR_INVALID_ARG),
+    ],
+)
+def test_create_rejects_bad_config(kw, code):
+    args = dict(num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=16, dtype="f32", num_workgroups=4, device=-1)
+    args.update(kw)
+    with pytest.raises(lib.BsrError) as e:
+        lib.BsrAttention(**args)
+    assert e.value.code == code

@@ -1,0 +1,187 @@
+"""HIP path against the CPU oracle, element by element (needs an MI355X)."""
+
+import numpy as np
+import pytest
+import torch
+
+from serving_attention_bsr_amd import lib
+from serving_attention_bsr_amd import workloads as W
+from tests.gpu_common import compare, handle_for, oracle_of, run_gpu, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _mfma_missing(exc):
+    return isinstance(exc, lib.BsrError) and exc.code == lib.BSR_ERR_UNSUPPORTED
+
+
+SWEEP = [
+    # name, qo_lens, kv_lens, h_qo, h_kv, d, P, dtype, causal, cap, nwg
+    ("f32_d64_p16", [1, 1, 1, 1], [17, 64, 100, 255], 8, 2, 64, 16, "f32", False, 0.0, 0),
+    ("f32_d64_split", [1, 1, 1, 1], [17, 64, 100, 255], 8, 2, 64, 16, "f32", False, 0.0, 64),
+    ("f32_d128_p3_cap", [1, 1, 1], [1, 77, 1000], 8, 4, 128, 3, "f32", False, 10.0, 0),
+    ("f32_d256_g1", [1, 1], [33, 500], 2, 2, 256, 16, "f32", False, 0.0, 0),
+    ("bf16_d128_p16", [1] * 9, [1, 2, 31, 32, 33, 511, 512, 513, 3000], 32, 8, 128, 16, "bf16", False, 0.0, 0),
+    ("bf16_d128_p1", [1] * 5, [7, 64, 129, 700, 2048], 32, 8, 128, 1, "bf16", False, 0.0, 0),
+    ("bf16_d128_p5_split", [1] * 5, [7, 64, 129, 700, 2048], 32, 8, 128, 5, "bf16", False, 0.0, 16),
+    ("bf16_d64_g8_rows8", [1, 1, 1], [100, 1000, 5], 16, 2, 64, 16, "bf16", False, 0.0, 0),
+    ("bf16_d256_g4_cap", [1] * 4, [64, 300, 512, 1500], 16, 4, 256, 16, "bf16", False, 30.0, 0),
+    ("bf16_d256_g2", [1] * 3, [10, 300, 900], 8, 4, 256, 7, "bf16", False, 0.0, 8),
+    ("bf16_spec2_causal", [2, 2, 2], [2, 90, 333], 8, 2, 128, 16, "bf16", True, 0.0, 0),
+    ("bf16_empty_rows", [1, 1, 1], [0, 40, 0], 8, 2, 128, 16, "bf16", False, 0.0, 0),
+    ("bf16_g1_cap_split", [1] * 4, [4000, 1, 63, 65], 4, 4, 128, 16, "bf16", False, 5.0, 4),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[c[0] for c in SWEEP])
+def test_sweep(case):
+    name, qo, kv, h_qo, h_kv, d, P, dtype, causal, cap, nwg = case
+    say("case", name)
+    w = W.build(name, 21, qo, kv, P, h_qo, h_kv, d, dtype=dtype, causal=causal, cap=cap)
+    o, lse, info = run_gpu(w, num_workgroups=nwg)
+    say("plan", info)
+    ro, rl = oracle_of(w)
+    compare(w, o, lse, ro, rl, name)
+
+
+@pytest.mark.parametrize("name", ["tiny_decode_f32", "batch_decode", "skewed_long_decode"])
+def test_named_decode(name):
+    say("workload", name)
+    w = W.named(name)
+    o, lse, info = run_gpu(w)
+    say("plan", info)
+    ro, rl = oracle_of(w)
+    compare(w, o, lse, ro, rl, name)
+
+
+def test_named_prefill():
+    say("workload ragged_causal_prefill")
+    w = W.named("ragged_causal_prefill")
+    try:
+        o, lse, info = run_gpu(w)
+    except lib.BsrError as exc:
+        if _mfma_missing(exc):
+            pytest.skip("MFMA tile body not built in this library")
+        raise
+    ro, rl = oracle_of(w)
+    compare(w, o, lse, ro, rl, "ragged_causal_prefill")
+
+
+def test_named_composable():
+    say("workload shared_prefix_composable")
+    w = W.named("shared_prefix_composable")
+    try:
+        o, lse, info = run_gpu(w, composable=True)
+    except lib.BsrError as exc:
+        if _mfma_missing(exc):
+            pytest.skip("MFMA tile body not built in this library")
+        raise
+    ro, rl = oracle_of(w, composable=True)
+    compare(w, o, lse, ro, rl, "shared_prefix_composable")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = W.named("skewed_long_decode", long_len=16384, n_short=7)
+    h = handle_for(w)
+    q, k, v, idx = to_gpu(w)
+    info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    assert info["num_partial_items"] > 0, "the case must exercise the merge"
+    o0, l0 = h.run(q, k, v, idx)
+    o0, l0 = o0.clone(), l0.clone()
+    for _ in range(10):
+        o, l = h.run(q, k, v, idx)
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16))
+        assert torch.equal(l.view(torch.int32), l0.view(torch.int32))
+    h.check()
+
+
+def test_physical_page_permutation_keeps_bits():
+    w = W.named("batch_decode", batch=16, lo=100, hi=3000)
+    o, lse, _ = run_gpu(w)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(w.k_pool.shape[0])  # new position of each page
+    inv = np.argsort(perm)
+    w2 = W.named("batch_decode", batch=16, lo=100, hi=3000)
+    w2.k_pool = w.k_pool[torch.from_numpy(inv)]
+    w2.v_pool = w.v_pool[torch.from_numpy(inv)]
+    w2.kv_indices = perm[w.kv_indices].astype(np.int32)
+    o2, lse2, _ = run_gpu(w2)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_graph_capture_replays_after_replan():
+    """A captured run() replays the current plan: re-plan new lengths, replay again."""
+    w1 = W.named("batch_decode", seed=31, batch=24, lo=64, hi=4000)
+    w2 = W.named("batch_decode", seed=32, batch=24, lo=64, hi=4000)
+    dev = torch.device("cuda:0")
+    n_pages = max(w1.k_pool.shape[0], w2.k_pool.shape[0])
+    n_idx = max(len(w1.kv_indices), len(w2.kv_indices))
+    q = torch.empty(w1.q.shape, dtype=w1.q.dtype, device=dev)
+    k = torch.empty((n_pages,) + tuple(w1.k_pool.shape[1:]), dtype=w1.k_pool.dtype, device=dev)
+    v = torch.empty_like(k)
+    idx = torch.zeros(n_idx, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    h = handle_for(w1, max_total_kv=int(max(w1.kv_lens.sum(), w2.kv_lens.sum())))
+
+    def load(w):
+        q.copy_(w.q)
+        k[: w.k_pool.shape[0]].copy_(w.k_pool)
+        v[: w.v_pool.shape[0]].copy_(w.v_pool)
+        idx[: len(w.kv_indices)].copy_(torch.from_numpy(np.ascontiguousarray(w.kv_indices)))
+        h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+        torch.cuda.synchronize()
+
+    load(w1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        h.run(q, k, v, idx, o, lse)  # warm the launch path outside capture
+    torch.cuda.synchronize()
+    eager_o, eager_l = o.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        h.run(q, k, v, idx, o, lse)
+    ro, rl = oracle_of(w1)
+    for rep in range(3):
+        o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), eager_o.view(torch.int16)), f"replay {rep} differs from eager"
+        compare(w1, o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, f"graph replay {rep}")
+    load(w2)
+    ro2, rl2 = oracle_of(w2)
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        compare(w2, o.double().cpu().numpy(), lse.double().cpu().numpy(), ro2, rl2, f"replan replay {rep}")
+    h.check()
+
+
+def test_merge_states_matches_oracle():
+    import oracle
+
+    rng = np.random.default_rng(3)
+    rows, d = 1000, 128
+    oa = rng.standard_normal((rows, d)).astype(np.float32)
+    ob = rng.standard_normal((rows, d)).astype(np.float32)
+    la = (rng.standard_normal(rows) * 5).astype(np.float32)
+    lb = (rng.standard_normal(rows) * 5).astype(np.float32)
+    la[:10] = -np.inf
+    lb[5:15] = -np.inf
+    oa[:10] = 0
+    ob[5:15] = 0
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(a).to(dev)
+    o, l = lib.merge_states(t(oa), t(la), t(ob), t(lb))
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge_state(oa, la, ob, lb)
+    np.testing.assert_allclose(o.cpu().numpy(), ro, atol=2e-6, rtol=2e-6)
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(l.cpu().numpy()))
+    np.testing.assert_allclose(l.cpu().numpy()[fin], rl[fin], atol=2e-6, rtol=2e-6)
+    # in place (output aliases the first input)
+    oa_t, la_t = t(oa), t(la)
+    lib.merge_states(oa_t, la_t, t(ob), t(lb), oa_t, la_t)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(oa_t.cpu().numpy(), ro, atol=2e-6, rtol=2e-6)

@@ -1,0 +1,208 @@
+"""The host planner, through a host-only handle of the real library (no GPU).
+
+* A CPU float64 executor runs the decoded plan (work items, then the merge map)
+  and must reproduce the oracle's result: every (query, key) pair is covered
+  exactly once and every merge reads states that were written.
+* Plan invariants from the pages (Core mechanism 6 and 7 of the FlashInfer
+  explainer page, paper Algorithm 1 and Appendix D.2/D.3): chunks never exceed
+  L_kv, only split work writes partial states, at most 2 * #workgroups partial
+  chunks, longest-first queues, byte-identical plans for identical lengths.
+* Validation errors are returned before anything is launched.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from serving_attention_bsr_amd import lib
+from serving_attention_bsr_amd import workloads as W
+from tests import plan_blob
+
+
+def host_handle(h_qo, h_kv, d, P, dtype="bf16", causal=False, cap=0.0, nwg=8, **kw):
+    args = dict(
+        num_qo_heads=h_qo, num_kv_heads=h_kv, head_dim=d, page_size=P, dtype=dtype, causal=causal,
+        logits_soft_cap=cap, num_workgroups=nwg, device=-1, max_batch=512, max_total_qo=1 << 16,
+        max_total_kv=1 << 24,
+    )
+    args.update(kw)
+    return lib.BsrAttention(**args)
+
+
+def f64(t):
+    return t.double().numpy()
+
+
+CASES = [
+    # name, qo_lens, kv_lens, h_qo, h_kv, d, P, dtype, causal, cap, nwg, min_chunk
+    ("decode_split", [1, 1, 1, 1], [17, 64, 100, 255], 8, 2, 64, 16, "f32", False, 0.0, 16, 64),
+    ("decode_one_wg", [1, 1, 1], [300, 5, 129], 8, 2, 64, 3, "f32", False, 0.0, 1, 64),
+    ("decode_cap_many_wg", [1] * 6, [700, 64, 65, 1, 300, 129], 4, 4, 64, 16, "bf16", False, 5.0, 32, 64),
+    ("spec_decode_rows8", [2, 2, 1], [200, 90, 333], 8, 2, 64, 5, "bf16", True, 0.0, 8, 64),
+    ("prefill_causal_tiles", [40, 7, 70], [100, 7, 200], 8, 2, 64, 1, "bf16", True, 0.0, 8, 64),
+    ("prefill_noncausal", [33, 1], [90, 450], 4, 1, 64, 2, "bf16", False, 2.0, 5, 64),
+    ("mixed_decode_prefill", [1, 50, 1, 3], [500, 120, 77, 3], 8, 2, 64, 4, "bf16", True, 0.0, 12, 64),
+    ("empty_rows", [1, 0, 1, 2], [0, 5, 70, 0], 4, 2, 64, 4, "bf16", False, 0.0, 4, 64),
+    ("fp32_long_queries", [20, 3], [40, 300], 8, 2, 64, 16, "f32", True, 0.0, 8, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_plan_executes_to_oracle(case):
+    name, qo, kv, h_qo, h_kv, d, P, dtype, causal, cap, nwg, min_chunk = case
+    w = W.build(name, 7, qo, kv, P, h_qo, h_kv, d, dtype=dtype, causal=causal, cap=cap)
+    h = host_handle(h_qo, h_kv, d, P, dtype, causal, cap, nwg, min_kv_chunk=min_chunk)
+    info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    plan = plan_blob.decode(h.plan_bytes())
+    assert plan["header"]["num_wg"] == nwg == info["num_workgroups"]
+    q, k, v = f64(w.q), f64(w.k_pool), f64(w.v_pool)
+    o, lse, written = plan_blob.execute(plan, q, k, v, w.kv_indices, w.group, P, w.scale, cap)
+    ro, rl = oracle.bsr_attention(
+        q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, P, h_qo, h_kv, w.scale, causal, cap
+    )
+    assert np.all(written == 1), "every (token, head) is written exactly once"
+    np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-12)
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], rl[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_plan_splits_and_merges_when_work_is_long():
+    w = W.build("split", 3, [1, 1], [5000, 64], 16, 8, 2, 64, dtype="bf16", tensors=False)
+    h = host_handle(8, 2, 64, 16, nwg=8)
+    info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    assert info["num_partial_items"] > 0 and info["num_merge_tasks"] == 2
+    plan = plan_blob.decode(h.plan_bytes())
+    partial = plan["items"]["flags"] & plan_blob.ITEM_PARTIAL != 0
+    # the short request is not split and writes directly (paper Appendix D.2)
+    short = plan["items"][(plan["items"]["qo_begin"] == 1)]
+    assert np.all(short["flags"] & plan_blob.ITEM_PARTIAL == 0)
+    assert np.all(plan["items"]["kv_end"][partial] - plan["items"]["kv_begin"][partial] <= info["kv_chunk"])
+
+
+def test_composable_plan_executes_to_oracle():
+    w = W.shared_prefix_composable(
+        seed=9, branches=6, prefix_len=48, suf_lo=1, suf_hi=40, page_size=16, num_qo_heads=8, num_kv_heads=2,
+        head_dim=64,
+    )
+    h = host_handle(8, 2, 64, 16, nwg=6)
+    fm = [f.as_dict() for f in w.formats]
+    info = h.plan_composable(fm, w.batch)
+    assert info["kernel"] == lib.KERNEL_MIXED
+    plan = plan_blob.decode(h.plan_bytes())
+    q, k, v = f64(w.q), f64(w.k_pool), f64(w.v_pool)
+    o, lse, written = plan_blob.execute(plan, q, k, v, w.kv_indices_formats, w.group, 16, w.scale, 0.0)
+    ro, rl = oracle.composable_attention(q, k, v, fm, w.kv_indices_formats, 16, 8, 2, w.scale)
+    assert np.all(written == 1)
+    np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-12)
+
+
+def unit_chunks(plan, group):
+    """Chunks grouped by (first token, head): list of (kv_begin, kv_end, partial)."""
+    units = {}
+    for it in plan["items"]:
+        key = (int(it["qo_begin"]), int(it["kv_head"]), int(it["page_begin"]))
+        units.setdefault(key, []).append(
+            (int(it["kv_begin"]), int(it["kv_end"]), bool(it["flags"] & plan_blob.ITEM_PARTIAL))
+        )
+    return units
+
+
+@pytest.mark.parametrize("name", ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill"])
+@pytest.mark.parametrize("nwg", [1, 64, 512])
+def test_named_workload_plan_invariants(name, nwg):
+    w = W.named(name, tensors=False)
+    h = host_handle(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype, w.causal, w.cap, nwg)
+    info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    plan = plan_blob.decode(h.plan_bytes())
+    items = plan["items"]
+    lens = items["kv_end"] - items["kv_begin"]
+    # chunks never exceed L_kv
+    assert np.all(lens <= info["kv_chunk"])
+    # L_kv follows the pages' formula, rounded to the KV granule (64) and at least 64
+    g = w.group
+    tile_tokens = max(1, info["q_tile"] // g)
+    total = 0
+    for lq, lk in zip(w.qo_lens, w.kv_lens):
+        for t0 in range(0, int(lq), tile_tokens):
+            nt = min(tile_tokens, int(lq) - t0)
+            eff = min(int(lk), int(lk) - int(lq) + t0 + nt) if w.causal else int(lk)
+            total += eff * w.num_kv_heads
+    expect = max(-(-max(-(-total // nwg), 1) // 64) * 64, 64)
+    assert info["kv_chunk"] == expect
+    # per unit: chunks tile [0, l_eff) without gaps; partial iff split
+    n_split_chunks = 0
+    for chunks in unit_chunks(plan, g).values():
+        chunks.sort()
+        assert chunks[0][0] == 0
+        for a, b in zip(chunks, chunks[1:]):
+            assert a[1] == b[0]
+        split = len(chunks) > 1
+        assert all(c[2] == split for c in chunks)
+        n_split_chunks += len(chunks) if split else 0
+    # partial-output bound of paper Appendix D.3: at most 2 * #workgroups chunks
+    assert n_split_chunks <= 2 * nwg
+    assert info["num_partial_items"] == n_split_chunks
+    # queues are longest-first
+    for wg in range(nwg):
+        q_items = items[plan["item_ptr"][wg] : plan["item_ptr"][wg + 1]]
+        cost = q_items["qo_count"] * g + (q_items["kv_end"] - q_items["kv_begin"])
+        assert np.all(np.diff(cost) <= 0)
+    # longest-processing-time bound on the busiest workgroup
+    assert info["max_wg_cost"] <= info["total_cost"] / nwg + (
+        max(int(lens.max()) + tile_tokens * g, 1) + 2 * g * int(max(1, (plan["merge"]["src_count"].max() if len(plan["merge"]) else 1)))
+    )
+    # determinism: same lengths, same bytes; the plan never sees page ids
+    first = h.plan_bytes()
+    h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    assert np.array_equal(first, h.plan_bytes())
+    h2 = host_handle(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype, w.causal, w.cap, nwg)
+    h2.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    assert np.array_equal(first, h2.plan_bytes())
+
+
+def test_kernel_choice_follows_query_tile_rule():
+    h = host_handle(32, 8, 128, 16, nwg=16)
+    assert h.plan([0, 1, 2], [0, 1, 2], [16, 16])["kernel"] == lib.KERNEL_DECODE
+    assert h.plan([0, 1, 2], [0, 1, 2], [16, 16])["q_tile"] == 4
+    assert h.plan([0, 2, 3], [0, 1, 2], [16, 16])["q_tile"] == 8
+    assert h.plan([0, 300], [0, 20], [16])["kernel"] == lib.KERNEL_MFMA
+    assert h.plan([0, 300, 301], [0, 20, 21], [16, 16])["kernel"] == lib.KERNEL_MIXED
+
+
+@pytest.mark.parametrize(
+    "qo, kv, last, causal, code",
+    [
+        ([0, 1, 0], [0, 1, 2], [3, 3], False, lib.BSR_ERR_INVALID_ARG),    # qo_indptr decreasing
+        ([0, 1, 2], [0, 2, 1], [3, 3], False, lib.BSR_ERR_INVALID_ARG),    # kv_indptr decreasing
+        ([0, 1, 2], [0, 1, 2], [0, 3], False, lib.BSR_ERR_INVALID_ARG),    # last_page_len < 1
+        ([0, 1, 2], [0, 1, 2], [3, 17], False, lib.BSR_ERR_INVALID_ARG),   # last_page_len > P
+        ([0, 5, 6], [0, 1, 2], [3, 3], True, lib.BSR_ERR_INVALID_ARG),     # causal l_qo > l_kv
+        ([1, 2, 3], [0, 1, 2], [3, 3], False, lib.BSR_ERR_INVALID_ARG),    # qo_indptr[0] != 0
+    ],
+)
+def test_plan_rejects_malformed(qo, kv, last, causal, code):
+    h = host_handle(8, 2, 64, 16, causal=causal)
+    with pytest.raises(lib.BsrError) as e:
+        h.plan(qo, kv, last)
+    assert e.value.code == code
+
+
+def test_plan_capacity_errors():
+    h = host_handle(8, 2, 64, 16, max_batch=2, max_total_qo=4, max_total_kv=100)
+    with pytest.raises(lib.BsrError) as e:
+        h.plan([0, 1, 2, 3], [0, 1, 2, 3], [1, 1, 1])
+    assert e.value.code == lib.BSR_ERR_CAPACITY
+    with pytest.raises(lib.BsrError) as e:
+        h.plan([0, 5], [0, 1], [1])
+    assert e.value.code == lib.BSR_ERR_CAPACITY
+    with pytest.raises(lib.BsrError) as e:
+        h.plan([0, 1], [0, 7], [16])
+    assert e.value.code == lib.BSR_ERR_CAPACITY
+
+
+def test_empty_batch_plans():
+    h = host_handle(8, 2, 64, 16)
+    info = h.plan([0], [0], [])
+    assert info["num_items"] == 0 and info["num_merge_tasks"] == 0
