@@ -15,6 +15,8 @@ prefill: TFLOP/s).  The CPU oracle is timed on the same host as a baseline.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +33,31 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 HEADLINE = "batch_decode"
 ALL = ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill", "shared_prefix_composable"]
+
+
+def kernel_source_hash():
+    """sha256 over the library's kernel and host sources, in path order."""
+    h = hashlib.sha256()
+    base = os.path.join(ROOT, "serving_attention_bsr_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(base, "**", "*"), recursive=True)):
+        if path.endswith((".h", ".hpp", ".hip", ".cpp")):
+            h.update(os.path.relpath(path, base).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch from the committed counter record of this workload, or
+    None when the record is missing or was taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes")
 
 
 def algorithmic_work(w, composable=False):
@@ -63,7 +90,18 @@ def algorithmic_work(w, composable=False):
     return dict(bytes=kv_bytes + qo_bytes + idx_bytes, kv_bytes=kv_bytes, flops=flops)
 
 
-def timed_steps(fn, steps, warmup, stream, flush):
+def flush_caches(flush, mode):
+    """Evict L2 and the Infinity Cache: read (default) leaves only clean lines behind,
+    so the timed kernel pays no write-back of the flush's own data."""
+    if flush is None or mode == "none":
+        return
+    if mode == "write":
+        flush.add_(1)
+    else:
+        flush.view(-1, 1 << 16).amax(dim=1)
+
+
+def timed_steps(fn, steps, warmup, stream, flush, mode="read"):
     """Per-step HIP-event times (ms) of fn(), each preceded by a cache flush."""
     import torch
 
@@ -74,8 +112,7 @@ def timed_steps(fn, steps, warmup, stream, flush):
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        if flush is not None:
-            flush.add_(1)
+        flush_caches(flush, mode)
         starts[i].record(stream)
         fn()
         ends[i].record(stream)
@@ -84,7 +121,7 @@ def timed_steps(fn, steps, warmup, stream, flush):
     return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]), wall
 
 
-def bench_workload(name, steps, warmup, flush, graph=True):
+def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
     import torch
 
     from serving_attention_bsr_amd import lib
@@ -101,20 +138,23 @@ def bench_workload(name, steps, warmup, flush, graph=True):
     h = lib.BsrAttention(
         w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, dtype=w.dtype, causal=w.causal,
         logits_soft_cap=w.cap, max_batch=max_batch, max_total_qo=int(w.qo_indptr[-1]),
-        max_total_kv=int(w.kv_lens.sum()), device=0,
+        max_total_kv=int(w.kv_lens.sum()), device=0, num_workgroups=nwg,
     )
     work = algorithmic_work(w, composable)
     out = dict(workload=name, dtype=w.dtype, bytes=work["bytes"], flops=work["flops"])
     try:
-        t0 = time.perf_counter()
-        reps = 20
-        for _ in range(reps):
+        torch.cuda.synchronize()
+        plan_times = []
+        for _ in range(20):
+            t0 = time.perf_counter()
             if composable:
                 info = h.plan_composable([f.as_dict() for f in w.formats], w.batch)
             else:
                 info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+            plan_times.append(time.perf_counter() - t0)
         torch.cuda.synchronize()
-        out["plan_us"] = (time.perf_counter() - t0) / reps * 1e6
+        out["plan_us"] = float(np.median(plan_times) * 1e6)
+        out["plan_us_first"] = float(plan_times[0] * 1e6)
     except lib.BsrError as exc:
         out["error"] = str(exc)
         return out, None
@@ -126,7 +166,7 @@ def bench_workload(name, steps, warmup, flush, graph=True):
     def step():
         h.run(q, k, v, idx, o, lse)
 
-    times, wall = timed_steps(step, steps, warmup, stream, flush)
+    times, wall = timed_steps(step, steps, warmup, stream, flush, mode)
     h.check()
     med = float(np.median(times))
     out["ms_median"] = med
@@ -149,7 +189,7 @@ def bench_workload(name, steps, warmup, flush, graph=True):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
                 step()
-            gt, _ = timed_steps(g.replay, steps, warmup, stream, flush)
+            gt, _ = timed_steps(g.replay, steps, warmup, stream, flush, mode)
             out["graph_ms_median"] = float(np.median(gt))
         except Exception as exc:  # report, do not hide
             out["graph_error"] = repr(exc)
@@ -198,6 +238,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--num-workgroups", type=int, default=0, help="persistent grid (0: device resident count)")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
@@ -216,7 +258,8 @@ def main():
     results = {}
     keep = {}
     for name in names:
-        r, ctx = bench_workload(name, args.steps, args.warmup, flush, graph=not args.no_graph)
+        r, ctx = bench_workload(name, args.steps, args.warmup, flush, graph=not args.no_graph,
+                                nwg=args.num_workgroups, mode=args.flush)
         results[name] = r
         print(f"[bench] {name}: {json.dumps({k: v for k, v in r.items() if k != 'plan'})}", file=sys.stderr, flush=True)
         if name == HEADLINE:
@@ -258,7 +301,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(HEADLINE),
         },
         "device": {"name": prof.name, "arch": getattr(prof, "gcnArchName", ""), "cus": prof.multi_processor_count},
         "workloads": {

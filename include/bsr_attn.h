@@ -97,12 +97,15 @@ typedef struct bsr_attn_config {
   int32_t max_batch;       /* most block rows of one plan (all formats together) */
   int32_t max_total_qo;    /* most query tokens (rows of Q) of one plan */
   int64_t max_total_kv;    /* most KV tokens summed over the block rows of one plan */
-  int32_t num_workgroups;  /* persistent grid size; 0 = what the device keeps resident */
+  int32_t num_workgroups;  /* persistent grid budget; each kernel uses at most what the
+                              device keeps resident; 0 = the kernel's default per CU */
   int32_t cost_alpha;      /* work-item cost weights alpha, beta; 0 selects 1 */
   int32_t cost_beta;
   int32_t min_kv_chunk;    /* smallest KV chunk the planner cuts, tokens; 0 selects 64 */
   int32_t max_partial_rows;/* partial-state capacity in folded rows; 0 = derived bound */
-  int32_t reserved[3];     /* must be 0 */
+  int32_t cost_item;       /* fixed cost of one work item, in KV-token units (pipeline
+                              fill and drain); 0 selects the default, < 0 selects none */
+  int32_t reserved[2];     /* must be 0 */
 } bsr_attn_config;
 
 /* One BSR sub-matrix for bsr_attn_plan_composable().  Arrays are host memory. */

@@ -40,17 +40,18 @@ def _run(cmd):
     return proc.returncode, "\n".join(lines)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, out_path: str = OUT, defines=(), build_dir: str = BUILD_DIR) -> str:
     """Compile every source and link the shared library; returns its path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
     jobs_list = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        jobs_list.append([hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        jobs_list.append([hipcc, *COMMON, *extra, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))
-        jobs_list.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src.replace(".cpp", ".o"))
+        jobs_list.append([hipcc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         results = list(ex.map(_run, jobs_list))
     failed = False
@@ -61,13 +62,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if failed:
         raise RuntimeError("HIP build failed")
     objs = [c[-1] for c in jobs_list]
-    tmp = OUT + ".tmp"
+    tmp = out_path + ".tmp"
     rc, out = _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     if rc != 0:
         sys.stderr.write(out + "\n")
         raise RuntimeError("link failed")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

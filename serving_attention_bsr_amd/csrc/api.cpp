@@ -63,7 +63,7 @@ struct DeviceGuard {
 
 namespace bsr {
 
-const void* find_kernel(const KernelKey& key) {
+const void* find_kernel(const KernelKey& key, int* wg_per_cu) {
   static std::vector<KernelEntry> table;
   static std::once_flag once;
   std::call_once(once, [] {
@@ -74,8 +74,10 @@ const void* find_kernel(const KernelKey& key) {
   for (const KernelEntry& e : table) {
     const KernelKey& k = e.key;
     if (k.kind == key.kind && k.bf16 == key.bf16 && k.head_dim == key.head_dim &&
-        k.rows == key.rows && k.cap == key.cap)
+        k.rows == key.rows && k.cap == key.cap) {
+      if (wg_per_cu != nullptr) *wg_per_cu = e.wg_per_cu;
       return e.fn;
+    }
   }
   return nullptr;
 }
@@ -86,7 +88,7 @@ struct bsr_attn {
   bsr_attn_config cfg;
   int device = -1;
   PlanConfig pc;
-  int32_t num_wg[4] = {0, 0, 0, 0};
+  int32_t num_wg[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};  // [kind][decode rows 4/8]
   int64_t plan_capacity = 0;
   int64_t partial_o_off = 0, partial_lse_off = 0, ws_bytes = 0;
   hipEvent_t upload_done = nullptr;
@@ -104,6 +106,8 @@ int validate_config(const bsr_attn_config* c) {
   if (c == nullptr) return fail(BSR_ERR_INVALID_ARG, "config is null");
   if (c->num_qo_heads <= 0 || c->num_kv_heads <= 0 || c->num_qo_heads % c->num_kv_heads != 0)
     return fail(BSR_ERR_INVALID_ARG, "num_qo_heads must be a positive multiple of num_kv_heads");
+  if (c->num_qo_heads / c->num_kv_heads > 16)
+    return fail(BSR_ERR_UNSUPPORTED, "at most 16 query heads per KV head are supported");
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
     return fail(BSR_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
   if (c->page_size < 1 || c->page_size > (1 << 16))
@@ -177,31 +181,26 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
     }
     const int cus = prop.multiProcessorCount;
     for (int kind = bsr::kKindDecode; kind <= bsr::kKindMixed; ++kind) {
-      int resident = -1;
-      const int rows_options[2] = {4, 8};
-      for (int ri = 0; ri < (kind == bsr::kKindMfma ? 1 : 2); ++ri) {
-        KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : rows_options[ri], cap};
-        const void* fn = bsr::find_kernel(key);
-        if (fn == nullptr) continue;
+      for (int ri = 0; ri < 2; ++ri) {
+        KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : (ri == 0 ? 4 : 8), cap};
+        int preferred = 1;
+        const void* fn = bsr::find_kernel(key, &preferred);
+        if (fn == nullptr) continue;  // instance not built for this configuration
         int per_cu = 0;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, bsr::kWgThreads, 0);
         if (e != hipSuccess) {
           delete h;
           return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
         }
-        resident = resident < 0 ? per_cu * cus : std::min(resident, per_cu * cus);
-      }
-      if (resident <= 0) continue;  // kernel kind not built for this configuration
-      if (cfg->num_workgroups > 0) {
-        if (cfg->num_workgroups > resident) {
-          delete h;
-          return fail(BSR_ERR_INVALID_ARG, "num_workgroups " + std::to_string(cfg->num_workgroups) +
-                                               " exceeds the " + std::to_string(resident) +
-                                               " workgroups the device keeps resident");
+        // the merge phase waits on other workgroups, so the grid never exceeds
+        // what stays resident; a caller's budget is capped per instance
+        const int resident = per_cu * cus;
+        if (resident <= 0) continue;
+        if (cfg->num_workgroups > 0) {
+          h->num_wg[kind][ri] = std::min(cfg->num_workgroups, resident);
+        } else {
+          h->num_wg[kind][ri] = std::min(per_cu, std::max(preferred, 1)) * cus;
         }
-        h->num_wg[kind] = cfg->num_workgroups;
-      } else {
-        h->num_wg[kind] = resident;
       }
     }
     e = hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming);
@@ -210,10 +209,10 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
       return hip_fail(e, "hipEventCreateWithFlags");
     }
   } else {
-    for (int kind = 1; kind <= 3; ++kind) h->num_wg[kind] = cfg->num_workgroups;
+    for (int kind = 1; kind <= 3; ++kind) h->num_wg[kind][0] = h->num_wg[kind][1] = cfg->num_workgroups;
   }
   int32_t max_wg = 1;
-  for (int kind = 1; kind <= 3; ++kind) max_wg = std::max(max_wg, h->num_wg[kind]);
+  for (int kind = 1; kind <= 3; ++kind) max_wg = std::max({max_wg, h->num_wg[kind][0], h->num_wg[kind][1]});
 
   PlanConfig& pc = h->pc;
   pc.h_qo = cfg->num_qo_heads;
@@ -223,10 +222,11 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.page_size = cfg->page_size;
   pc.causal = cfg->causal != 0;
   pc.bf16 = bf16;
-  for (int k = 0; k < 4; ++k) pc.num_wg[k] = h->num_wg[k];
+  for (int k = 0; k < 4; ++k) pc.num_wg[k][0] = h->num_wg[k][0], pc.num_wg[k][1] = h->num_wg[k][1];
   pc.alpha = cfg->cost_alpha > 0 ? cfg->cost_alpha : 1;
   pc.beta = cfg->cost_beta > 0 ? cfg->cost_beta : 1;
   pc.min_chunk = cfg->min_kv_chunk > 0 ? cfg->min_kv_chunk : 64;
+  pc.gamma = cfg->cost_item > 0 ? cfg->cost_item : (cfg->cost_item < 0 ? 0 : 512);
   pc.max_batch = cfg->max_batch;
   pc.max_total_qo = cfg->max_total_qo;
   pc.max_total_kv = cfg->max_total_kv;
@@ -252,6 +252,9 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   h->partial_o_off = h->plan_capacity;
   h->partial_lse_off = align_up(h->partial_o_off + pc.max_partial_rows * cfg->head_dim * 4, 256);
   h->ws_bytes = align_up(h->partial_lse_off + pc.max_partial_rows * 4, 256);
+#ifdef BSR_TRACE
+  h->ws_bytes += align_up(int64_t(max_wg) * 64, 256);  // 8 stamps per workgroup
+#endif
 
   bsr::RunParams& p = h->params;
   std::memset(&p, 0, sizeof(p));
@@ -268,6 +271,9 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   p.cap_log2 = cfg->logits_soft_cap * 1.4426950408889634f;
   p.partial_o_off = h->partial_o_off;
   p.partial_lse_off = h->partial_lse_off;
+#ifdef BSR_TRACE
+  p.trace_off = align_up(h->partial_lse_off + pc.max_partial_rows * 4, 256);
+#endif
   *out = h;
   return BSR_OK;
 }
@@ -293,7 +299,7 @@ static int finish_plan(bsr_attn_t h, std::vector<BlockRow>& rows, int32_t total_
   if (h->device >= 0) {
     fn = bsr::find_kernel(KernelKey{res.kernel, h->pc.bf16, h->pc.head_dim, rows_key,
                                     h->cfg.logits_soft_cap > 0.0f});
-    if (fn == nullptr || h->num_wg[res.kernel] <= 0)
+    if (fn == nullptr)
       return fail(BSR_ERR_UNSUPPORTED, "no kernel built for this plan's kind " + std::to_string(res.kernel));
   }
   DeviceGuard guard(h->device);

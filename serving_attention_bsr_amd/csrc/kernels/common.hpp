@@ -82,18 +82,6 @@ __device__ __forceinline__ int32_t* plan_i32(uint8_t* ws, int32_t off) {
   return reinterpret_cast<int32_t*>(ws + off);
 }
 
-// Publish a ready stamp after this workgroup's partial-state stores: every thread
-// makes its own stores visible device-wide, the workgroup meets, then one thread
-// releases the stamp.
-__device__ __forceinline__ void publish_flag(int32_t* flag, int32_t epoch) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 constexpr int kMaxSpins = 1 << 21;
 
 // Wait (bounded) until *flag == epoch.  Returns false if the bound expired.

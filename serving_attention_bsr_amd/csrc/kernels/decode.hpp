@@ -19,9 +19,10 @@
 //
 // Page gather (Core mechanism 1, paper section 3.1.1): key tau of the block row
 // is slot tau % P of page kv_indices[page_begin + tau / P].  Page ids are loaded
-// two steps ahead of the K/V rows, and K/V one step ahead of the arithmetic, so
-// a wavefront always has a full step of KV loads in flight.  Keys past the chunk
-// are clamped to its last key and masked, so no unused slot is ever read.
+// three steps ahead of the arithmetic and K/V rows two steps ahead, so a
+// wavefront keeps two steps of KV loads in flight while it computes.  Keys past
+// the chunk are clamped to its last key and masked, so no unused slot is ever
+// read.
 #pragma once
 
 #include "common.hpp"
@@ -40,8 +41,7 @@ struct DecodeBody {
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
 
   struct Pids {
-    int32_t page[TB];
-    int32_t slot[TB];
+    uint32_t row[TB];  // KV row index in the pool: (page * H_kv + head) * P + slot
   };
   struct Kv {
     uint4 k[TB][NLD];
@@ -60,8 +60,10 @@ struct DecodeBody {
       int tau = it.kv_begin + tile * TILE + i * NG + grp;
       tau = min(tau, it.kv_end - 1);
       const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
-      out.slot[i] = tau - static_cast<int32_t>(pl) * p.page_size;
-      out.page[i] = p.kv_indices[it.page_begin + static_cast<int32_t>(pl)];
+      const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+      const uint32_t page = static_cast<uint32_t>(p.kv_indices[it.page_begin + static_cast<int32_t>(pl)]);
+      out.row[i] = (page * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head)) *
+                       static_cast<uint32_t>(p.page_size) + slot;
     }
   }
 
@@ -71,9 +73,7 @@ struct DecodeBody {
     const uint8_t* vb = static_cast<const uint8_t*>(p.v_pool);
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
-      const int64_t row =
-          (static_cast<int64_t>(ids.page[i]) * p.h_kv + it.kv_head) * p.page_size + ids.slot[i];
-      const int64_t off = row * (D * ESZ) + c * 16;
+      const uint64_t off = static_cast<uint64_t>(ids.row[i]) * (D * ESZ) + c * 16;
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         out.k[i][j] = *reinterpret_cast<const uint4*>(kb + off + j * (LPT * 16));
@@ -123,9 +123,11 @@ struct DecodeBody {
     }
   }
 
+  // One tile of keys.  live = false masks every key: the update is then an exact
+  // no-op (alpha = 1, p = 0 against finite values).
   static __device__ __forceinline__ void step(const RunParams& p, const WorkItem& it, int tile,
-                                              int grp, const uint4 (&q)[ROWS][NLD], const Kv& kv,
-                                              State& st) {
+                                              int grp, bool live, const uint4 (&q)[ROWS][NLD],
+                                              const Kv& kv, State& st) {
     float s[TB][ROWS];
 #pragma unroll
     for (int i = 0; i < TB; ++i)
@@ -135,7 +137,7 @@ struct DecodeBody {
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
       const int tau = it.kv_begin + tile * TILE + i * NG + grp;
-      const bool in_chunk = tau < it.kv_end;
+      const bool in_chunk = live && tau < it.kv_end;
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         float x;
@@ -183,7 +185,7 @@ struct DecodeBody {
   template <typename Emit>
   static __device__ void run(const RunParams& p, const WorkItem& it, float* lds, Emit&& emit) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps loops scalar
     const int c = lane % LPT;
     const int grp = lane / LPT;
     const int g = p.group;
@@ -217,24 +219,48 @@ struct DecodeBody {
       for (int e = 0; e < 16; ++e) st.acc[r][e] = 0.0f;
     }
 
+    // Tiles wave, wave + 4, ... of the item; local tile j of this wavefront.
+    // Pipeline (issue order is what the in-order load counter sees): step j
+    // issues the page ids of tile j+3, then K/V of tile j+2 (its ids arrived a
+    // step ago, and were issued before K/V of tile j+1, so waiting for them
+    // leaves tile j+1 in flight), then computes tile j.  The loop starts at
+    // j = -3 with every key masked while j < 0, so every load is issued and
+    // consumed by the one loop body on every path (a separate prologue, or a
+    // branch around the arithmetic, would leave loads pending into registers
+    // the loop head reuses and force a full wait there).  The id buffers start
+    // at the row of the chunk's first key, and loads past the end are clamped to
+    // its last key, so every load is in bounds and no load sits behind a branch.
     const int ntok = it.kv_end - it.kv_begin;
     const int ntiles = (ntok + TILE - 1) / TILE;
-    int t = wave;
-    Pids pa, pb;
-    Kv ka, kb;
-    if (t < ntiles) load_pids(p, it, t, grp, pa);
-    if (t + kWaves < ntiles) load_pids(p, it, t + kWaves, grp, pb);
-    if (t < ntiles) load_kv(p, it, c, pa, ka);
-    while (t < ntiles) {
-      if (t + kWaves < ntiles) load_kv(p, it, c, pb, kb);
-      if (t + 2 * kWaves < ntiles) load_pids(p, it, t + 2 * kWaves, grp, pa);
-      step(p, it, t, grp, q, ka, st);
-      t += kWaves;
-      if (t >= ntiles) break;
-      if (t + kWaves < ntiles) load_kv(p, it, c, pa, ka);
-      if (t + 2 * kWaves < ntiles) load_pids(p, it, t + 2 * kWaves, grp, pb);
-      step(p, it, t, grp, q, kb, st);
-      t += kWaves;
+    const int nt_w = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+    if (nt_w > 0) {
+      Pids p0, p1, p2;
+      Kv k0 = {}, k1 = {}, k2 = {};  // warm-up steps read these before any load lands
+      {
+        const uint32_t first = p.kv_indices[it.page_begin + it.kv_begin / p.page_size];
+        const uint32_t row0 = (first * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head)) *
+                                  static_cast<uint32_t>(p.page_size) +
+                              static_cast<uint32_t>(it.kv_begin % p.page_size);
+#pragma unroll
+        for (int i = 0; i < TB; ++i) p2.row[i] = row0;
+      }
+      const int t0 = wave;
+      int j = -3;
+      asm volatile("" : "+s"(j));  // keep the warm-up steps inside the loop
+      while (true) {
+        load_pids(p, it, t0 + (j + 3) * kWaves, grp, p0);
+        load_kv(p, it, c, p2, k2);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k0, st);
+        if (++j >= nt_w) break;
+        load_pids(p, it, t0 + (j + 3) * kWaves, grp, p1);
+        load_kv(p, it, c, p0, k0);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k1, st);
+        if (++j >= nt_w) break;
+        load_pids(p, it, t0 + (j + 3) * kWaves, grp, p2);
+        load_kv(p, it, c, p1, k1);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k2, st);
+        if (++j >= nt_w) break;
+      }
     }
 
     // ⊕ across the lane groups of this wavefront (lanes differing in bits >= log2(LPT))

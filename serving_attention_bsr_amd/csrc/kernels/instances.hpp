@@ -8,14 +8,30 @@ namespace bsr {
 
 // KV rows per lane group per wavefront step: two for bf16; one for fp32, whose
 // rows take twice the registers.
+#ifndef BSR_DECODE_TB
+#define BSR_DECODE_TB 2
+#endif
+#ifndef BSR_DECODE_OCC
+#define BSR_DECODE_OCC 1
+#endif
 template <bool BF16>
-constexpr int kDecodeTb = BF16 ? 2 : 1;
+constexpr int kDecodeTb = BF16 ? BSR_DECODE_TB : 1;
+
+// Workgroups per CU the register allocation must allow.
+template <int D, bool BF16, int ROWS>
+constexpr int kDecodeOcc = (BF16 && ROWS == 4) ? BSR_DECODE_OCC : 1;
+// Default grid of the decode body: one workgroup per CU.  The KV stream is
+// bound by the chip's bandwidth, not by per-CU latency hiding, and a second
+// workgroup per CU only shortens chunks (more partial states) and shares the CU.
+constexpr int kDecodeWgPerCu = 1;
 
 template <int D, bool BF16, int ROWS, bool CAP>
 inline void add_decode(std::vector<KernelEntry>* out) {
   out->push_back({KernelKey{kKindDecode, BF16, D, ROWS, CAP},
                   reinterpret_cast<const void*>(
-                      &bsr_persistent_kernel<D, BF16, ROWS, kDecodeTb<BF16>, CAP, kKindDecode>)});
+                      &bsr_persistent_kernel<D, BF16, ROWS, kDecodeTb<BF16>, CAP, kKindDecode,
+                                             kDecodeOcc<D, BF16, ROWS>>),
+                  kDecodeWgPerCu});
 }
 
 template <int D>

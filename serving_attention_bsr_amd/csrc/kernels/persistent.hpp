@@ -8,9 +8,10 @@
 // the same kernel, in the order the plan fixed, without atomic accumulation.
 //
 // Ordering between a partial's writer and its merger uses release/acquire ready
-// stamps, not read-modify-write: the writer stores the run's epoch into the
-// partial's flag after its stores; the merger waits until the flag equals the
-// epoch.  Each workgroup keeps its own run counter in the plan blob; the plan
+// stamps, not read-modify-write: after its attention items a workgroup releases
+// once and stores the run's epoch into the flag of each partial state it wrote;
+// a merging workgroup waits until the flags of its sources equal the epoch, then
+// acquires once.  Each workgroup keeps its own run counter in the plan blob; the plan
 // upload zeroes all counters and every run advances each by one, so all
 // workgroups of a run agree on its epoch and stamps of older runs never match.
 // Every workgroup finishes its attention items before it merges, and the grid
@@ -29,11 +30,27 @@ template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND>
 struct PersistentKernel {
   using Decode = DecodeBody<D, BF16, ROWS, TB, CAP>;
   using Merge = MergeBody<D, BF16>;
-  static constexpr int LDS_FLOATS = Decode::LDS_FLOATS;
+  static constexpr int LDS_FLOATS =
+      Decode::LDS_FLOATS > Merge::LDS_FLOATS ? Decode::LDS_FLOATS : Merge::LDS_FLOATS;
 };
 
-template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND>
-__global__ __launch_bounds__(kWgThreads) void bsr_persistent_kernel(RunParams p) {
+// Optional per-workgroup timeline (compile with BSR_TRACE): wall-clock stamps at
+// phase boundaries, stored after the partial-state segments of the workspace.
+#ifdef BSR_TRACE
+#define BSR_STAMP(k)                                                                         \
+  do {                                                                                       \
+    if (threadIdx.x == 0)                                                                    \
+      reinterpret_cast<uint64_t*>(ws + p.trace_off)[wg * 8 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define BSR_STAMP(k) \
+  do {               \
+  } while (0)
+#endif
+
+// OCC: workgroups per CU the register allocation must allow.
+template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, int OCC>
+__global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunParams p) {
   using K = PersistentKernel<D, BF16, ROWS, TB, CAP, KIND>;
   __shared__ float lds[K::LDS_FLOATS];
   __shared__ int32_t s_epoch;
@@ -45,6 +62,7 @@ __global__ __launch_bounds__(kWgThreads) void bsr_persistent_kernel(RunParams p)
   int32_t* epochs = plan_i32(ws, hdr->off_epochs);
   int32_t* flags = plan_i32(ws, hdr->off_flags);
   int32_t* status = plan_i32(ws, hdr->off_status);
+  BSR_STAMP(0);
   if (threadIdx.x == 0) s_epoch = epochs[wg] + 1;
   __syncthreads();
   const int32_t epoch = s_epoch;
@@ -54,6 +72,7 @@ __global__ __launch_bounds__(kWgThreads) void bsr_persistent_kernel(RunParams p)
   const int32_t* item_ptr = plan_i32(ws, hdr->off_item_ptr);
   const WorkItem* items = reinterpret_cast<const WorkItem*>(ws + hdr->off_items);
   const int32_t ib = item_ptr[wg], ie = item_ptr[wg + 1];
+  bool any_partial = false;
   for (int32_t i = ib; i < ie; ++i) {
     const WorkItem it = items[i];
     if (it.flags & kItemPartial) {
@@ -65,7 +84,7 @@ __global__ __launch_bounds__(kWgThreads) void bsr_persistent_kernel(RunParams p)
         if (d == 0) pl[row] = lse2;
       };
       K::Decode::run(p, it, lds, emit);
-      publish_flag(flags + it.flag_id, epoch);
+      any_partial = true;
     } else {
       auto emit = [&](int r, int d, float o0, float o1, float lse2) {
         const int64_t orow =
@@ -81,15 +100,42 @@ __global__ __launch_bounds__(kWgThreads) void bsr_persistent_kernel(RunParams p)
     }
   }
 
+  BSR_STAMP(1);
+  // One release for all partial states this workgroup wrote (a release writes
+  // back the XCD's L2, so it is done once per workgroup, not per item): every
+  // wavefront releases its own stores, the workgroup meets, wavefront 0 releases
+  // again (covering what the barrier ordered before it) and stores the stamps.
+  if (any_partial) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      for (int32_t i = ib + static_cast<int32_t>(threadIdx.x); i < ie; i += 64) {
+        const WorkItem& it = items[i];
+        if (it.flags & kItemPartial)
+          __hip_atomic_store(flags + it.flag_id, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+
+  BSR_STAMP(2);
   // ---- contraction of partial states -----------------------------------------
   const int32_t* merge_ptr = plan_i32(ws, hdr->off_merge_ptr);
   const MergeTask* tasks = reinterpret_cast<const MergeTask*>(ws + hdr->off_merge);
   const MergeSrc* srcs = reinterpret_cast<const MergeSrc*>(ws + hdr->off_srcs);
   const int32_t mb = merge_ptr[wg], me = merge_ptr[wg + 1];
-  const int wave = threadIdx.x >> 6;
+  // the workgroup waits for every source of its tasks (one thread per source),
+  // acquires once, then merges its tasks one after another
   bool ok = true;
-  for (int32_t t = mb + wave; t < me; t += kWaves) ok = K::Merge::run(p, tasks[t], srcs, flags, epoch) && ok;
-  if (!ok && (threadIdx.x & 63) == 0) status[kStatusWaitTimeout] = 1;
+  if (mb < me) {
+    for (int32_t t = mb; t < me && ok; ++t) ok = K::Merge::wait(tasks[t], srcs, flags, epoch);
+    BSR_STAMP(3);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+    for (int32_t t = mb; t < me; ++t) K::Merge::run(p, tasks[t], srcs, lds);
+  }
+  BSR_STAMP(4);
+  if (!ok) status[kStatusWaitTimeout] = 1;
 
   __syncthreads();
   if (threadIdx.x == 0) epochs[wg] = epoch;

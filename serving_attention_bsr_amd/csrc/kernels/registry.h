@@ -9,7 +9,8 @@ namespace bsr {
 
 struct KernelEntry {
   KernelKey key;
-  const void* fn;  // host stub of __global__ void(RunParams)
+  const void* fn;     // host stub of __global__ void(RunParams)
+  int wg_per_cu;      // default grid: this many workgroups per CU (if resident)
 };
 
 // Each instance file appends its kernels.

@@ -26,6 +26,7 @@ struct RunParams {
   float cap_inv;
   float cap_log2;       // cap * log2(e)
   int32_t pad;
+  int64_t trace_off;    // workspace offset of the optional timeline (trace builds only)
 };
 
 struct KernelKey {
@@ -36,7 +37,8 @@ struct KernelKey {
   bool cap;
 };
 
-// Host stub of the matching persistent kernel, or null if not built.
-const void* find_kernel(const KernelKey& key);
+// Host stub of the matching persistent kernel, or null if not built; the
+// instance's preferred workgroups per CU go to *wg_per_cu when non-null.
+const void* find_kernel(const KernelKey& key, int* wg_per_cu = nullptr);
 
 }  // namespace bsr

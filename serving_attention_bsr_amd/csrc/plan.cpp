@@ -13,13 +13,19 @@
 //      granule and at least the minimum chunk;
 //   4. units longer than L_kv are cut into equal chunks of at most L_kv; only
 //      those write partial states, the rest write O/LSE directly;
-//   5. cost = alpha * rows + beta * KV tokens; items sorted by cost, longest
-//      first, each given to the least-loaded workgroup (min-heap on
-//      (load, workgroup id)), so the plan depends on the lengths only;
+//   5. cost = alpha * rows + beta * KV tokens (+ gamma, a fixed per-item cost
+//      that models pipeline fill and drain; an extension of the pages' model);
+//      items sorted by cost, longest first, each given to the least-loaded
+//      workgroup (min-heap on (load, workgroup id)), so the plan depends on the
+//      lengths only;
 //   6. partial states get fixed slots; every query token whose result is split
 //      gets a merge task listing its partial states in KV order (format order
 //      first for composed formats), and merge tasks are spread the same way.
-// Ties are broken by creation order, so equal lengths give identical bytes.
+// Steps 4-6 are evaluated for L_kv and for L_kv / k (k <= kChunkCandidates); the
+// plan with the smallest predicted makespan is kept, the pages' L_kv unless a
+// finer cut is better by more than 3 % (finer cuts help when indivisible short
+// units leave some workgroups over-full).  Ties are broken by creation order, so
+// equal lengths give identical bytes.
 #include "plan.h"
 
 #include <algorithm>
@@ -77,6 +83,226 @@ void assign_longest_first(const std::vector<int64_t>& costs, std::vector<int64_t
   }
 }
 
+struct Schedule {
+  int64_t chunk = 0;
+  std::vector<Item> items;
+  std::vector<MergeTask> tasks;
+  std::vector<MergeSrc> srcs;
+  std::vector<int32_t> owner, order, mowner, morder;
+  int64_t partial_rows = 0;
+  int32_t num_flags = 0, num_partial_items = 0;
+  int64_t makespan = 0, total = 0;
+};
+
+// Steps 4-7 for one chunk length: items, direct/partial, merge map, assignment.
+// fill = false: the pages' rule -- units longer than `chunk` are cut into equal
+// chunks of at most `chunk`, then every item goes longest-first to the least
+// loaded workgroup.  fill = true: units of at most `chunk` keys (the ones the
+// pages leave whole) go longest-first to the least-loaded workgroup first; then
+// each longer unit, longest first, is cut into pieces that fill the least-loaded
+// workgroup up to the mean load (Stream-K-like filling, no piece below the
+// minimum chunk), so indivisible short units no longer leave some workgroups
+// over-full.
+int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std::vector<Unit>& units,
+             int64_t chunk, bool fill, int32_t nwg, int32_t total_qo, bool composable, Schedule* out,
+             std::string* err) {
+  (void)err;
+  const int32_t g = cfg.group;
+  const int32_t h_kv = cfg.h_kv;
+  const int64_t min_piece = round_up(std::max(cfg.min_chunk, 1), kChunkGranule);
+  auto template_of = [&](int32_t ui) {
+    const Unit& u = units[ui];
+    const BlockRow& r = rows[u.row];
+    WorkItem w;
+    std::memset(&w, 0, sizeof(w));
+    w.flags = u.mfma ? kItemMfma : 0;
+    w.qo_begin = r.qo_begin + u.t0;
+    w.qo_count = u.nt;
+    w.kv_head = u.head;
+    w.page_begin = r.page_begin;
+    w.causal_limit = u.causal_limit;
+    w.partial_row = -1;
+    w.flag_id = -1;
+    return w;
+  };
+  auto item_cost = [&](int32_t ui, int64_t keys) {
+    return cfg.alpha * static_cast<int64_t>(units[ui].nt) * g + cfg.beta * keys + cfg.gamma;
+  };
+
+  // ---- 4. chunks -> items, and 7a. their assignment --------------------------
+  std::vector<Item> items;
+  items.reserve(units.size() + 2 * nwg);
+  std::vector<int64_t> load(nwg, 0);
+  std::vector<int32_t> owner, order;
+  if (!fill) {
+    for (int32_t ui = 0; ui < static_cast<int32_t>(units.size()); ++ui) {
+      const Unit& u = units[ui];
+      WorkItem w = template_of(ui);
+      if (u.l_eff == 0) {
+        if (composable) continue;  // contributes no keys to the composed result
+        items.push_back({w, item_cost(ui, 0), ui, 1});
+        continue;
+      }
+      const int64_t n = ceil_div(u.l_eff, chunk);
+      const int64_t csz = n == 1 ? u.l_eff : round_up(ceil_div(u.l_eff, n), kChunkGranule);
+      for (int64_t b = 0; b < u.l_eff; b += csz) {
+        w.kv_begin = static_cast<int32_t>(b);
+        w.kv_end = static_cast<int32_t>(std::min<int64_t>(b + csz, u.l_eff));
+        items.push_back({w, item_cost(ui, w.kv_end - w.kv_begin), ui, 0});
+      }
+    }
+    std::vector<int64_t> costs(items.size());
+    for (size_t i = 0; i < items.size(); ++i) costs[i] = items[i].cost;
+    assign_longest_first(costs, &load, &owner, &order);
+  } else {
+    std::vector<int32_t> short_u, long_u;
+    int64_t total = 0;
+    for (int32_t ui = 0; ui < static_cast<int32_t>(units.size()); ++ui) {
+      const Unit& u = units[ui];
+      if (u.l_eff == 0 && composable) continue;
+      (u.l_eff <= chunk ? short_u : long_u).push_back(ui);
+      total += item_cost(ui, u.l_eff);
+    }
+    // filling cuts about one piece per workgroup beyond one per long unit
+    if (!long_u.empty()) total += cfg.gamma * nwg;
+    auto longer = [&](int32_t a, int32_t b) { return units[a].l_eff > units[b].l_eff; };
+    std::stable_sort(short_u.begin(), short_u.end(), longer);
+    std::stable_sort(long_u.begin(), long_u.end(), longer);
+    const int64_t target = ceil_div(total, nwg);
+    using Slot = std::pair<int64_t, int32_t>;
+    std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+    for (int32_t w = 0; w < nwg; ++w) heap.push({0, w});
+    auto place = [&](int32_t ui, int64_t b, int64_t e) {
+      Slot s = heap.top();
+      heap.pop();
+      WorkItem w = template_of(ui);
+      w.kv_begin = static_cast<int32_t>(b);
+      w.kv_end = static_cast<int32_t>(e);
+      const int64_t c = item_cost(ui, e - b);
+      order.push_back(static_cast<int32_t>(items.size()));
+      owner.push_back(s.second);
+      items.push_back({w, c, ui, 0});
+      s.first += c;
+      load[s.second] = s.first;
+      heap.push(s);
+    };
+    for (int32_t ui : short_u) place(ui, 0, units[ui].l_eff);
+    for (int32_t ui : long_u) {
+      const int64_t len = units[ui].l_eff;
+      int64_t pos = 0;
+      while (pos < len) {
+        const int64_t rem = len - pos;
+        const int64_t fixed = item_cost(ui, 0);
+        const int64_t space = target - heap.top().first - fixed;
+        // pieces round up to the granule (the rounding overshoot is absorbed by
+        // workgroups that end up with no long piece) and are never tiny
+        const int64_t floor_piece = std::max<int64_t>(min_piece, 4 * kChunkGranule);
+        // and at most twice L_kv (the fixed item cost makes a full workgroup hold
+        // a little more than L_kv keys)
+        const int64_t cap = 2 * chunk;
+        int64_t piece = std::min(rem, cap);
+        if (piece > space) {
+          piece = std::min(cap, std::max(floor_piece, round_up(std::max<int64_t>(space, 0), kChunkGranule)));
+          if (rem - piece < floor_piece && rem <= cap) piece = rem;
+        }
+        place(ui, pos, pos + piece);
+        pos += piece;
+      }
+    }
+    // queues run in assignment order: owner/order already follow it
+  }
+  {
+    std::vector<int32_t> count(units.size(), 0);
+    for (const Item& it : items) count[it.unit] += 1;
+    for (Item& it : items) it.nchunks = count[it.unit];
+  }
+
+  // ---- 5. direct write versus partial ----------------------------------------
+  // (token, head) coverage counts; an item writes O/LSE directly when its unit is
+  // not split and it is the only contributor for every token it covers.
+  std::vector<int32_t> cover(static_cast<size_t>(total_qo) * h_kv, 0);
+  for (const Item& it : items)
+    for (int32_t t = 0; t < it.w.qo_count; ++t)
+      cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] += 1;
+  int64_t partial_rows = 0;
+  int32_t num_flags = 0, num_partial_items = 0;
+  for (Item& it : items) {
+    bool direct = it.nchunks == 1;
+    for (int32_t t = 0; direct && t < it.w.qo_count; ++t)
+      direct = cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] == 1;
+    if (!direct) {
+      it.w.flags |= kItemPartial;
+      it.w.partial_row = static_cast<int32_t>(partial_rows);
+      it.w.flag_id = num_flags++;
+      partial_rows += static_cast<int64_t>(it.w.qo_count) * g;
+      ++num_partial_items;
+    }
+  }
+
+  // ---- 6. merge map ----------------------------------------------------------
+  // A (token, head) needs a merge task unless a direct item wrote it.
+  std::vector<std::vector<MergeSrc>> srcs_of(static_cast<size_t>(total_qo) * h_kv);
+  std::vector<char> written(static_cast<size_t>(total_qo) * h_kv, 0);
+  std::vector<char> needed(static_cast<size_t>(total_qo) * h_kv, 0);
+  for (const Item& it : items) {
+    for (int32_t t = 0; t < it.w.qo_count; ++t) {
+      const size_t key = static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head;
+      if (it.w.flags & kItemPartial)
+        srcs_of[key].push_back({it.w.partial_row + t * g, it.w.flag_id});
+      else
+        written[key] = 1;
+    }
+  }
+  if (composable) {
+    // tokens a format lists must end up with a result even if no key covers them
+    for (const BlockRow& r : rows)
+      for (int32_t t = 0; t < r.qo_len; ++t)
+        for (int32_t h = 0; h < h_kv; ++h) needed[static_cast<size_t>(r.qo_begin + t) * h_kv + h] = 1;
+  }
+  std::vector<MergeTask> tasks;
+  std::vector<MergeSrc> srcs;
+  for (size_t key = 0; key < srcs_of.size(); ++key) {
+    if (written[key]) continue;
+    if (srcs_of[key].empty() && !needed[key]) continue;
+    MergeTask m;
+    m.qo_row = static_cast<int32_t>(key / h_kv);
+    m.kv_head = static_cast<int32_t>(key % h_kv);
+    m.src_begin = static_cast<int32_t>(srcs.size());
+    m.src_count = static_cast<int32_t>(srcs_of[key].size());
+    srcs.insert(srcs.end(), srcs_of[key].begin(), srcs_of[key].end());
+    tasks.push_back(m);
+  }
+
+  // ---- 7b. merge tasks, longest first, on top of the attention loads ---------
+  std::vector<int64_t> mcosts(tasks.size());
+  for (size_t i = 0; i < tasks.size(); ++i)
+    mcosts[i] = cfg.gamma + cfg.beta * static_cast<int64_t>(tasks[i].src_count) * g;
+  std::vector<int32_t> mowner, morder;
+  assign_longest_first(mcosts, &load, &mowner, &morder);
+  out->makespan = 0;
+  out->total = 0;
+  for (int64_t l : load) {
+    out->makespan = std::max(out->makespan, l);
+    out->total += l;
+  }
+  // the longest chunk actually cut (L_kv for the pages' rule; filling may cut more)
+  out->chunk = chunk;
+  for (const Item& it : items)
+    if (it.nchunks > 1) out->chunk = std::max<int64_t>(out->chunk, it.w.kv_end - it.w.kv_begin);
+  out->partial_rows = partial_rows;
+  out->num_flags = num_flags;
+  out->num_partial_items = num_partial_items;
+  out->items = std::move(items);
+  out->tasks = std::move(tasks);
+  out->srcs = std::move(srcs);
+  out->owner = std::move(owner);
+  out->order = std::move(order);
+  out->mowner = std::move(mowner);
+  out->morder = std::move(morder);
+  return BSR_OK;
+
+}
+
 }  // namespace
 
 int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t total_qo,
@@ -129,10 +355,10 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       q_tile = tile;
     }
   }
-  const int32_t nwg = cfg.num_wg[kernel];
+  const int32_t nwg = cfg.num_wg[kernel][kernel != kKindMfma && decode_rows == 8 ? 1 : 0];
   if (nwg <= 0) {
-    *err = "no workgroup count for the selected kernel";
-    return BSR_ERR_INVALID_ARG;
+    *err = "the kernel this plan needs (kind " + std::to_string(kernel) + ") is not built for this handle";
+    return BSR_ERR_UNSUPPORTED;
   }
 
   // ---- 2. work units ---------------------------------------------------------
@@ -163,125 +389,48 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
     }
   }
 
-  // ---- 3. maximum KV chunk ---------------------------------------------------
+  // ---- 3. maximum KV chunk (the pages' L_kv) and its refinements -------------
   int64_t total_kv = 0;
   for (const Unit& u : units) total_kv += u.l_eff;
-  int64_t chunk = round_up(std::max<int64_t>(ceil_div(total_kv, nwg), 1), kChunkGranule);
-  chunk = std::max<int64_t>(chunk, round_up(std::max(cfg.min_chunk, 1), kChunkGranule));
-
-  // ---- 4. chunks -> items ----------------------------------------------------
-  std::vector<Item> items;
-  items.reserve(units.size() + 2 * nwg);
-  for (int32_t ui = 0; ui < static_cast<int32_t>(units.size()); ++ui) {
-    const Unit& u = units[ui];
-    const BlockRow& r = rows[u.row];
-    WorkItem w;
-    std::memset(&w, 0, sizeof(w));
-    w.flags = u.mfma ? kItemMfma : 0;
-    w.qo_begin = r.qo_begin + u.t0;
-    w.qo_count = u.nt;
-    w.kv_head = u.head;
-    w.page_begin = r.page_begin;
-    w.causal_limit = u.causal_limit;
-    w.partial_row = -1;
-    w.flag_id = -1;
-    const int64_t frows = static_cast<int64_t>(u.nt) * g;
-    if (u.l_eff == 0) {
-      if (composable) continue;  // contributes no keys to the composed result
-      w.kv_begin = 0;
-      w.kv_end = 0;
-      items.push_back({w, cfg.alpha * frows, ui, 1});
-      continue;
-    }
-    const int64_t n = ceil_div(u.l_eff, chunk);
-    const int64_t csz = n == 1 ? u.l_eff : round_up(ceil_div(u.l_eff, n), kChunkGranule);
-    int32_t made = 0;
-    for (int64_t b = 0; b < u.l_eff; b += csz) {
-      w.kv_begin = static_cast<int32_t>(b);
-      w.kv_end = static_cast<int32_t>(std::min<int64_t>(b + csz, u.l_eff));
-      items.push_back({w, cfg.alpha * frows + cfg.beta * (w.kv_end - w.kv_begin), ui, 0});
-      ++made;
-    }
-    for (int32_t k = 0; k < made; ++k) items[items.size() - 1 - k].nchunks = made;
-  }
-
-  // ---- 5. direct write versus partial ----------------------------------------
-  // (token, head) coverage counts; an item writes O/LSE directly when its unit is
-  // not split and it is the only contributor for every token it covers.
-  std::vector<int32_t> cover(static_cast<size_t>(total_qo) * h_kv, 0);
-  for (const Item& it : items)
-    for (int32_t t = 0; t < it.w.qo_count; ++t)
-      cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] += 1;
-  int64_t partial_rows = 0;
-  int32_t num_flags = 0, num_partial_items = 0;
-  for (Item& it : items) {
-    bool direct = it.nchunks == 1;
-    for (int32_t t = 0; direct && t < it.w.qo_count; ++t)
-      direct = cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] == 1;
-    if (!direct) {
-      it.w.flags |= kItemPartial;
-      it.w.partial_row = static_cast<int32_t>(partial_rows);
-      it.w.flag_id = num_flags++;
-      partial_rows += static_cast<int64_t>(it.w.qo_count) * g;
-      ++num_partial_items;
+  const int64_t min_chunk = round_up(std::max(cfg.min_chunk, 1), kChunkGranule);
+  const int64_t base_chunk =
+      std::max<int64_t>(round_up(std::max<int64_t>(ceil_div(total_kv, nwg), 1), kChunkGranule), min_chunk);
+  Schedule best;
+  bool have = false;
+  int64_t last_chunk = -1;
+  for (int k = 1; k <= kChunkCandidates + 1; ++k) {
+    // candidates: the pages' L_kv, L_kv / k (k = 2..), then filling at L_kv
+    const bool fill = k == kChunkCandidates + 1;
+    const int64_t chunk =
+        fill ? base_chunk : std::max<int64_t>(round_up(ceil_div(base_chunk, k), kChunkGranule), min_chunk);
+    if (!fill && chunk == last_chunk) continue;
+    last_chunk = chunk;
+    Schedule cand;
+    int rc = schedule(cfg, rows, units, chunk, fill, nwg, total_qo, composable, &cand, err);
+    if (rc != BSR_OK) return rc;
+    if (!have || cand.makespan * 100 < best.makespan * 97) {
+      best = std::move(cand);
+      have = true;
     }
   }
-  if (partial_rows > cfg.max_partial_rows) {
-    *err = "plan needs " + std::to_string(partial_rows) + " partial rows, capacity is " +
+  if (best.partial_rows > cfg.max_partial_rows) {
+    *err = "plan needs " + std::to_string(best.partial_rows) + " partial rows, capacity is " +
            std::to_string(cfg.max_partial_rows);
     return BSR_ERR_CAPACITY;
   }
-
-  // ---- 6. merge map ----------------------------------------------------------
-  // A (token, head) needs a merge task unless a direct item wrote it.
-  std::vector<std::vector<MergeSrc>> srcs_of(static_cast<size_t>(total_qo) * h_kv);
-  std::vector<char> written(static_cast<size_t>(total_qo) * h_kv, 0);
-  std::vector<char> needed(static_cast<size_t>(total_qo) * h_kv, 0);
-  for (const Item& it : items) {
-    for (int32_t t = 0; t < it.w.qo_count; ++t) {
-      const size_t key = static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head;
-      if (it.w.flags & kItemPartial)
-        srcs_of[key].push_back({it.w.partial_row + t * g, it.w.flag_id});
-      else
-        written[key] = 1;
-    }
-  }
-  if (composable) {
-    // tokens a format lists must end up with a result even if no key covers them
-    for (const BlockRow& r : rows)
-      for (int32_t t = 0; t < r.qo_len; ++t)
-        for (int32_t h = 0; h < h_kv; ++h) needed[static_cast<size_t>(r.qo_begin + t) * h_kv + h] = 1;
-  }
-  std::vector<MergeTask> tasks;
-  std::vector<MergeSrc> srcs;
-  for (size_t key = 0; key < srcs_of.size(); ++key) {
-    if (written[key]) continue;
-    if (srcs_of[key].empty() && !needed[key]) continue;
-    MergeTask m;
-    m.qo_row = static_cast<int32_t>(key / h_kv);
-    m.kv_head = static_cast<int32_t>(key % h_kv);
-    m.src_begin = static_cast<int32_t>(srcs.size());
-    m.src_count = static_cast<int32_t>(srcs_of[key].size());
-    srcs.insert(srcs.end(), srcs_of[key].begin(), srcs_of[key].end());
-    tasks.push_back(m);
-  }
-
-  // ---- 7. longest-first assignment -------------------------------------------
-  std::vector<int64_t> load(nwg, 0);
-  std::vector<int64_t> costs(items.size());
-  for (size_t i = 0; i < items.size(); ++i) costs[i] = items[i].cost;
-  std::vector<int32_t> owner, order;
-  assign_longest_first(costs, &load, &owner, &order);
-  std::vector<int64_t> mcosts(tasks.size());
-  for (size_t i = 0; i < tasks.size(); ++i)
-    mcosts[i] = cfg.alpha + cfg.beta * static_cast<int64_t>(tasks[i].src_count) * g;
-  std::vector<int32_t> mowner, morder;
-  assign_longest_first(mcosts, &load, &mowner, &morder);
-  int64_t max_load = 0, total_cost = 0;
-  for (int64_t l : load) {
-    max_load = std::max(max_load, l);
-    total_cost += l;
-  }
+  const std::vector<Item>& items = best.items;
+  const std::vector<MergeTask>& tasks = best.tasks;
+  const std::vector<MergeSrc>& srcs = best.srcs;
+  const std::vector<int32_t>& owner = best.owner;
+  const std::vector<int32_t>& order = best.order;
+  const std::vector<int32_t>& mowner = best.mowner;
+  const std::vector<int32_t>& morder = best.morder;
+  const int64_t chunk = best.chunk;
+  const int64_t partial_rows = best.partial_rows;
+  const int32_t num_flags = best.num_flags;
+  const int32_t num_partial_items = best.num_partial_items;
+  const int64_t max_load = best.makespan;
+  const int64_t total_cost = best.total;
 
   // ---- 8. blob ---------------------------------------------------------------
   PlanHeader hdr;

@@ -19,8 +19,10 @@ struct PlanConfig {
   int32_t h_qo = 0, h_kv = 0, group = 0, head_dim = 0, page_size = 0;
   bool causal = false;
   bool bf16 = false;
-  int32_t num_wg[4] = {0, 0, 0, 0};  // grid per KernelKind (index 1..3)
+  // grid per kernel instance: [KernelKind][decode rows 4 -> 0, 8 -> 1]
+  int32_t num_wg[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
   int64_t alpha = 1, beta = 1;
+  int64_t gamma = 512;       // fixed cost of a work item or merge task (KV-token units)
   int32_t min_chunk = 64;
   // capacities (plan rejected beyond them)
   int32_t max_batch = 0, max_total_qo = 0;
@@ -49,6 +51,9 @@ struct PlanResult {
 constexpr int kMaxDecodeRows = 8;
 // KV granularity that chunk lengths are rounded to (tokens).
 constexpr int kChunkGranule = 64;
+// The planner also tries L_kv / k for k up to this and keeps the smallest
+// predicted makespan (the pages' L_kv unless another is clearly better).
+constexpr int kChunkCandidates = 4;
 // MFMA tile heights (folded rows) the kernels implement, smallest first.
 constexpr int kMfmaTiles[] = {128};
 

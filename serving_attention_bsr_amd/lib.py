@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbsr_attn.so")
+LIB_PATH = os.environ.get("BSR_ATTN_LIBRARY") or os.path.join(HERE, "libbsr_attn.so")
 
 BSR_OK = 0
 BSR_ERR_INVALID_ARG = 1
@@ -70,7 +70,8 @@ class bsr_attn_config(ctypes.Structure):
         ("cost_beta", ctypes.c_int32),
         ("min_kv_chunk", ctypes.c_int32),
         ("max_partial_rows", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("cost_item", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -256,6 +257,7 @@ class BsrAttention:
         cost_beta: int = 0,
         min_kv_chunk: int = 0,
         max_partial_rows: int = 0,
+        cost_item: int = 0,
     ):
         cfg = bsr_attn_config()
         cfg.num_qo_heads = num_qo_heads
@@ -274,6 +276,7 @@ class BsrAttention:
         cfg.cost_beta = cost_beta
         cfg.min_kv_chunk = min_kv_chunk
         cfg.max_partial_rows = max_partial_rows
+        cfg.cost_item = cost_item
         self.cfg = cfg
         self.dtype = dtype
         self.device = device

@@ -120,7 +120,9 @@ def test_named_workload_plan_invariants(name, nwg):
     lens = items["kv_end"] - items["kv_begin"]
     # chunks never exceed L_kv
     assert np.all(lens <= info["kv_chunk"])
-    # L_kv follows the pages' formula, rounded to the KV granule (64) and at least 64
+    # L_kv follows the pages' formula (rounded to the 64-key granule, at least 64);
+    # the planner keeps it, a refinement L_kv / k (k <= 4), or filling at L_kv
+    # (pieces up to 2 L_kv), whichever predicts the smallest makespan
     g = w.group
     tile_tokens = max(1, info["q_tile"] // g)
     total = 0
@@ -129,10 +131,14 @@ def test_named_workload_plan_invariants(name, nwg):
             nt = min(tile_tokens, int(lq) - t0)
             eff = min(int(lk), int(lk) - int(lq) + t0 + nt) if w.causal else int(lk)
             total += eff * w.num_kv_heads
-    expect = max(-(-max(-(-total // nwg), 1) // 64) * 64, 64)
-    assert info["kv_chunk"] == expect
+    pages_lkv = max(-(-max(-(-total // nwg), 1) // 64) * 64, 64)
+    candidates = {max(-(-(-(-pages_lkv // k)) // 64) * 64, 64) for k in range(1, 5)}
+    filled = info["kv_chunk"] not in candidates
+    if filled:
+        assert pages_lkv <= info["kv_chunk"] <= 2 * pages_lkv
     # per unit: chunks tile [0, l_eff) without gaps; partial iff split
     n_split_chunks = 0
+    n_split_units = 0
     for chunks in unit_chunks(plan, g).values():
         chunks.sort()
         assert chunks[0][0] == 0
@@ -141,18 +147,28 @@ def test_named_workload_plan_invariants(name, nwg):
         split = len(chunks) > 1
         assert all(c[2] == split for c in chunks)
         n_split_chunks += len(chunks) if split else 0
-    # partial-output bound of paper Appendix D.3: at most 2 * #workgroups chunks
-    assert n_split_chunks <= 2 * nwg
+        n_split_units += int(split)
+    # partial-output bound of paper Appendix D.3 (2 * #workgroups chunks at the
+    # pages' L_kv; at a chunk L it reads 2 * sum / L)
+    if filled:
+        # filling cuts about one piece per workgroup plus one tail per split unit
+        assert n_split_chunks <= 2 * nwg + n_split_units
+    else:
+        assert n_split_chunks <= 2 * -(-total // info["kv_chunk"])
+        if info["kv_chunk"] == pages_lkv:
+            assert n_split_chunks <= 2 * nwg
     assert info["num_partial_items"] == n_split_chunks
-    # queues are longest-first
+    # queues are longest-first (cost = rows + keys + the fixed item cost 512);
+    # with filling, the unsplit units come first, longest first
     for wg in range(nwg):
         q_items = items[plan["item_ptr"][wg] : plan["item_ptr"][wg + 1]]
-        cost = q_items["qo_count"] * g + (q_items["kv_end"] - q_items["kv_begin"])
+        if filled:
+            q_items = q_items[(q_items["flags"] & plan_blob.ITEM_PARTIAL) == 0]
+        cost = q_items["qo_count"] * g + (q_items["kv_end"] - q_items["kv_begin"]) + 512
         assert np.all(np.diff(cost) <= 0)
     # longest-processing-time bound on the busiest workgroup
-    assert info["max_wg_cost"] <= info["total_cost"] / nwg + (
-        max(int(lens.max()) + tile_tokens * g, 1) + 2 * g * int(max(1, (plan["merge"]["src_count"].max() if len(plan["merge"]) else 1)))
-    )
+    max_task = 512 + g * int(plan["merge"]["src_count"].max()) if len(plan["merge"]) else 0
+    assert info["max_wg_cost"] <= info["total_cost"] / nwg + max(int(lens.max()) + tile_tokens * g + 512, max_task)
     # determinism: same lengths, same bytes; the plan never sees page ids
     first = h.plan_bytes()
     h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
