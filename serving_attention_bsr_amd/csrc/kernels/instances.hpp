@@ -34,8 +34,37 @@ inline void add_decode(std::vector<KernelEntry>* out) {
                   kDecodeWgPerCu});
 }
 
+// MFMA kernels: one workgroup per CU by default (the register and LDS use of the
+// MFMA body allow what the occupancy query reports).
+#ifndef BSR_MFMA_OCC
+#define BSR_MFMA_OCC 1
+#endif
+constexpr int kMfmaWgPerCu = BSR_MFMA_OCC;
+
+template <int D, bool CAP>
+inline void add_mfma(std::vector<KernelEntry>* out) {
+  out->push_back({KernelKey{kKindMfma, true, D, 0, CAP},
+                  reinterpret_cast<const void*>(
+                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, BSR_MFMA_OCC>),
+                  kMfmaWgPerCu});
+}
+
+template <int D, int ROWS, bool CAP>
+inline void add_mixed(std::vector<KernelEntry>* out) {
+  out->push_back({KernelKey{kKindMixed, true, D, ROWS, CAP},
+                  reinterpret_cast<const void*>(
+                      &bsr_persistent_kernel<D, true, ROWS, kDecodeTb<true>, CAP, kKindMixed, 1>),
+                  1});
+}
+
 template <int D>
 inline void register_head_dim(std::vector<KernelEntry>* out) {
+  add_mfma<D, false>(out);
+  add_mfma<D, true>(out);
+  add_mixed<D, 4, false>(out);
+  add_mixed<D, 4, true>(out);
+  add_mixed<D, 8, false>(out);
+  add_mixed<D, 8, true>(out);
   add_decode<D, true, 4, false>(out);
   add_decode<D, true, 4, true>(out);
   add_decode<D, true, 8, false>(out);

@@ -23,15 +23,38 @@
 #include "common.hpp"
 #include "decode.hpp"
 #include "merge.hpp"
+#include "prefill.hpp"
 
 namespace bsr {
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// KIND selects the attention bodies: decode only, MFMA only (bf16), or both
+// (chosen per work item).
 template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND>
 struct PersistentKernel {
+  static_assert(KIND == kKindDecode || BF16, "the MFMA body is bf16 only");
   using Decode = DecodeBody<D, BF16, ROWS, TB, CAP>;
+  using Mfma = MfmaBody<D, CAP>;
   using Merge = MergeBody<D, BF16>;
   static constexpr int LDS_FLOATS =
-      Decode::LDS_FLOATS > Merge::LDS_FLOATS ? Decode::LDS_FLOATS : Merge::LDS_FLOATS;
+      cmax(Merge::LDS_FLOATS, cmax(KIND == kKindMfma ? 0 : Decode::LDS_FLOATS,
+                                   KIND == kKindDecode ? 0 : Mfma::LDS_FLOATS));
+
+  template <typename Emit>
+  static __device__ __forceinline__ void attend(const RunParams& p, const WorkItem& it, float* lds,
+                                                Emit&& emit) {
+    if constexpr (KIND == kKindDecode) {
+      Decode::run(p, it, lds, emit);
+    } else if constexpr (KIND == kKindMfma) {
+      Mfma::run(p, it, lds, emit);
+    } else {
+      if (it.flags & kItemMfma)
+        Mfma::run(p, it, lds, emit);
+      else
+        Decode::run(p, it, lds, emit);
+    }
+  }
 };
 
 // Optional per-workgroup timeline (compile with BSR_TRACE): wall-clock stamps at
@@ -83,7 +106,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
         *reinterpret_cast<float2*>(po + row * D + d) = make_float2(o0, o1);
         if (d == 0) pl[row] = lse2;
       };
-      K::Decode::run(p, it, lds, emit);
+      K::attend(p, it, lds, emit);
       any_partial = true;
     } else {
       auto emit = [&](int r, int d, float o0, float o1, float lse2) {
@@ -96,7 +119,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
         }
         if (d == 0 && p.lse != nullptr) p.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
       };
-      K::Decode::run(p, it, lds, emit);
+      K::attend(p, it, lds, emit);
     }
   }
 

@@ -1,0 +1,284 @@
+// prefill.hpp -- MFMA attention body for work items with many folded query rows.
+//
+// Core mechanism 3 of the FlashInfer explainer page (paper section 3.2): scattered
+// KV tiles are gathered into contiguous on-chip tiles, after which sparse and
+// dense share one dense body.  Core mechanism 4 (paper section 3.2.2): tiles of at
+// least 16 query rows use the matrix cores.  Terms "GQA head-group fusion" (paper
+// Appendix A): the g query heads of a KV head are folded into the query rows, so a
+// tile of 128 folded rows is 128/g tokens and one KV tile serves all of them.
+// Reproduction section (paper section 4.2): prefill runs with a causal mask.
+//
+// gfx950 mapping.  A workgroup (4 wavefronts) owns 128 folded rows; wavefront w
+// owns rows 32w..32w+31.  Per tile of 64 keys:
+//   * the workgroup gathers the keys' K and V rows page by page (16-byte loads,
+//     one tile ahead, page ids two tiles ahead) and stages them in LDS: K row-major
+//     [key][D], V transposed [D][key] in the key order the P operand needs;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = the
+//     wavefront's Q rows, held in registers for the whole item): each lane then
+//     holds one query column and 16 keys of each 32-key block, so the softmax max
+//     and sums are in-lane (plus one exchange between the two lane halves);
+//   * base-2 online softmax, soft-cap and the causal mask (only on tiles that
+//     cross the diagonal or the chunk end);
+//   * O^T += V^T P^T: the probabilities, converted to bf16, are the B operand in
+//     exactly the registers the S^T result left them in, because V^T is stored
+//     with its keys permuted to match; A = V^T from LDS.
+// The result leaves through the same emit callback as the decode body.
+#pragma once
+
+#include "common.hpp"
+
+namespace bsr {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int D, bool CAP>
+struct MfmaBody {
+  static constexpr int BR = 128;           // folded rows per item
+  static constexpr int BC = 64;            // keys per tile
+  static constexpr int KB = BC / 32;       // 32-key blocks per tile
+  static constexpr int DK = D / 16;        // MFMA k-steps over D for S^T
+  static constexpr int DB = D / 32;        // 32-row blocks of O^T
+  static constexpr int KPAD = D + 8;       // K row stride in LDS (bf16)
+  static constexpr int VPAD = BC + 8;      // V^T row stride in LDS (bf16)
+  static constexpr int NQ = BC / 4;        // key quads per tile
+  static constexpr int NCH = D / 8;        // 8-element chunks per row
+  static constexpr int TASKS = NQ * NCH;   // (quad, chunk) load tasks per tile
+  static constexpr int TPT = (TASKS + kWgThreads - 1) / kWgThreads;  // tasks per thread
+  static constexpr int LDS_BYTES = BC * KPAD * 2 + D * VPAD * 2;
+  static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
+  static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+
+  // Position of key quad qd (0..BC/4) in the V^T row: within each 32-key block the
+  // k-index of the P operand is 16 s + 8 h + j, holding key quad 4 s + h + 2 (j/4).
+  static __device__ __forceinline__ int quad_pos(int qd) {
+    const int blk = qd >> 3, q = qd & 7;
+    return 32 * blk + 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
+  }
+
+  struct Loads {
+    uint4 k[TPT][4];
+    uint4 v[TPT][4];
+  };
+  struct Rows {
+    uint32_t row[TPT][4];
+  };
+
+  static __device__ __forceinline__ void task_of(int i, int& qd, int& ch) {
+    const int task = threadIdx.x + i * kWgThreads;
+    qd = task / NCH;
+    ch = task % NCH;
+  }
+
+  static __device__ __forceinline__ void load_rows(const RunParams& p, const WorkItem& it, int tile,
+                                                   Rows& out) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      int qd, ch;
+      task_of(i, qd, ch);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int tau = it.kv_begin + tile * BC + 4 * qd + j;
+        tau = min(tau, it.kv_end - 1);
+        const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+        const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+        const uint32_t page = static_cast<uint32_t>(p.kv_indices[it.page_begin + static_cast<int32_t>(pl)]);
+        out.row[i][j] = (page * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head)) *
+                            static_cast<uint32_t>(p.page_size) + slot;
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void load_kv(const RunParams& p, const Rows& rows, Loads& out) {
+    const uint8_t* kb = static_cast<const uint8_t*>(p.k_pool);
+    const uint8_t* vb = static_cast<const uint8_t*>(p.v_pool);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      int qd, ch;
+      task_of(i, qd, ch);
+      if (TASKS % kWgThreads != 0 && qd >= NQ) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint64_t off = static_cast<uint64_t>(rows.row[i][j]) * (D * 2) + ch * 16;
+        out.k[i][j] = *reinterpret_cast<const uint4*>(kb + off);
+        out.v[i][j] = *reinterpret_cast<const uint4*>(vb + off);
+      }
+    }
+  }
+
+  // K row-major; V transposed with each key quad's four keys packed in 8 bytes.
+  static __device__ __forceinline__ void store_lds(const Loads& in, uint16_t* lk, uint16_t* lv) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      int qd, ch;
+      task_of(i, qd, ch);
+      if (TASKS % kWgThreads != 0 && qd >= NQ) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(lk + (4 * qd + j) * KPAD + 8 * ch) = in.k[i][j];
+      const int pos = quad_pos(qd);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = e < 2 ? in.v[i][j].x : e < 4 ? in.v[i][j].y : e < 6 ? in.v[i][j].z : in.v[i][j].w;
+          h[j] = (e & 1) ? (w >> 16) : (w & 0xffffu);
+        }
+        uint2 packed;
+        packed.x = h[0] | (h[1] << 16);
+        packed.y = h[2] | (h[3] << 16);
+        *reinterpret_cast<uint2*>(lv + (8 * ch + e) * VPAD + pos) = packed;
+      }
+    }
+  }
+
+  template <typename Emit>
+  static __device__ void run(const RunParams& p, const WorkItem& it, float* lds_f, Emit&& emit) {
+    uint16_t* lk = reinterpret_cast<uint16_t*>(lds_f);
+    uint16_t* lv = lk + BC * KPAD;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31;    // query column of this lane
+    const int half = lane >> 5;   // lane half: which 4-row groups of each 8
+    const int g = p.group;
+    const int rows_valid = it.qo_count * g;
+    const int rho = wave * 32 + col;                  // folded row of this lane's column
+    const bool row_ok = rho < rows_valid;
+    const int t_local = rho / g;
+
+    // Q rows of this wavefront as the B operand: Q[rho][16 ks + 8 half + 0..7]
+    bf16x8_t qreg[DK];
+    {
+      const uint16_t* qb = static_cast<const uint16_t*>(p.q);
+      const int64_t qrow = static_cast<int64_t>(it.qo_begin + t_local) * p.h_qo + it.kv_head * g + rho % g;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row_ok) v = *reinterpret_cast<const uint4*>(qb + qrow * D + 16 * ks + 8 * half);
+        qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+
+    f32x16_t acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    float m_run = kNegInf;   // running max (base-2 units), shared by both lane halves
+    float l_run = 0.0f;      // this half's share of the running sum
+
+    const int ntok = it.kv_end - it.kv_begin;
+    const int ntiles = (ntok + BC - 1) / BC;
+    Rows rows_next;
+    Loads regs;
+    if (ntiles > 0) {
+      load_rows(p, it, 0, rows_next);
+      load_kv(p, rows_next, regs);
+      load_rows(p, it, 1 < ntiles ? 1 : 0, rows_next);
+    }
+    for (int t = 0; t < ntiles; ++t) {
+      __syncthreads();  // every wavefront is done reading the previous tile
+      store_lds(regs, lk, lv);
+      if (t + 1 < ntiles) {
+        load_kv(p, rows_next, regs);
+        load_rows(p, it, t + 2 < ntiles ? t + 2 : t + 1, rows_next);
+      }
+      __syncthreads();
+
+      // S^T = K Q^T, two 32-key blocks
+      f32x16_t s[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4*>(lk + (32 * kb + col) * KPAD + 16 * ks + 8 * half));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
+        }
+      }
+
+      // logits in base 2, soft-cap, masks
+      const int tile_base = it.kv_begin + t * BC;
+      const bool need_mask = tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit;
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x;
+          if constexpr (CAP) {
+            x = p.cap_log2 * tanh_exp(s[kb][r] * p.sm_scale * p.cap_inv);
+          } else {
+            x = s[kb][r] * p.scale_log2;
+          }
+          if (need_mask) {
+            const int tau = tile_base + 32 * kb + (r >> 2) * 8 + 4 * half + (r & 3);
+            if (tau >= it.kv_end || tau > it.causal_limit + t_local) x = kNegInf;
+          }
+          s[kb][r] = x;
+          mx = __builtin_fmaxf(mx, x);
+        }
+      }
+      mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32));
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float m_use = m_new == kNegInf ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.0f;
+      bf16x8_t pb[KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(s[kb][r] - m_use);
+          psum += e;
+          pb[kb][r >> 3][r & 7] = static_cast<__bf16>(e);
+        }
+      }
+      l_run = l_run * alpha + psum;
+      if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const bf16x8_t a = __builtin_bit_cast(
+                bf16x8_t,
+                *reinterpret_cast<const uint4*>(lv + (32 * db + col) * VPAD + 32 * kb + 16 * st + 8 * half));
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][st], acc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // result: this lane's column holds O^T[d][rho] for d = 32 db + 8 (r/4) + 4 half + r%4
+    const float l_tot = l_run + shfl_xor_f(l_run, 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse2 = l_tot > 0.0f ? m_run + fast_log2(l_tot) : kNegInf;
+    if (row_ok) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d = 32 * db + 8 * rq + 4 * half;
+          emit(rho, d, acc[db][4 * rq] * inv, acc[db][4 * rq + 1] * inv, lse2);
+          emit(rho, d + 2, acc[db][4 * rq + 2] * inv, acc[db][4 * rq + 3] * inv, lse2);
+        }
+      }
+    }
+    __syncthreads();  // LDS free for the next item
+  }
+};
+
+}  // namespace bsr
