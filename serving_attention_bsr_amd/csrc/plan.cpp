@@ -220,15 +220,20 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
   // ---- 5. direct write versus partial ----------------------------------------
   // (token, head) coverage counts; an item writes O/LSE directly when its unit is
   // not split and it is the only contributor for every token it covers.
-  std::vector<int32_t> cover(static_cast<size_t>(total_qo) * h_kv, 0);
-  for (const Item& it : items)
-    for (int32_t t = 0; t < it.w.qo_count; ++t)
-      cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] += 1;
+  // In a single format the units partition (token, head), so only composed
+  // formats need the coverage counts.
+  std::vector<int32_t> cover;
+  if (composable) {
+    cover.assign(static_cast<size_t>(total_qo) * h_kv, 0);
+    for (const Item& it : items)
+      for (int32_t t = 0; t < it.w.qo_count; ++t)
+        cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] += 1;
+  }
   int64_t partial_rows = 0;
   int32_t num_flags = 0, num_partial_items = 0;
   for (Item& it : items) {
     bool direct = it.nchunks == 1;
-    for (int32_t t = 0; direct && t < it.w.qo_count; ++t)
+    for (int32_t t = 0; composable && direct && t < it.w.qo_count; ++t)
       direct = cover[static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head] == 1;
     if (!direct) {
       it.w.flags |= kItemPartial;
@@ -240,36 +245,53 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
   }
 
   // ---- 6. merge map ----------------------------------------------------------
-  // A (token, head) needs a merge task unless a direct item wrote it.
-  std::vector<std::vector<MergeSrc>> srcs_of(static_cast<size_t>(total_qo) * h_kv);
-  std::vector<char> written(static_cast<size_t>(total_qo) * h_kv, 0);
-  std::vector<char> needed(static_cast<size_t>(total_qo) * h_kv, 0);
-  for (const Item& it : items) {
+  // A (token, head) needs a merge task unless a direct item wrote it; its sources
+  // are the partial states covering it, in item creation order (format, then KV
+  // order).  Built as a flat CSR over (token, head).
+  const size_t nkeys = (num_partial_items > 0 || composable) ? static_cast<size_t>(total_qo) * h_kv : 0;
+  std::vector<int32_t> src_ptr(nkeys + 1, 0);
+  std::vector<char> state(nkeys, 0);  // 1 = written directly, 2 = needs a task
+  for (const Item& it : (nkeys > 0 ? items : std::vector<Item>())) {
     for (int32_t t = 0; t < it.w.qo_count; ++t) {
       const size_t key = static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head;
-      if (it.w.flags & kItemPartial)
-        srcs_of[key].push_back({it.w.partial_row + t * g, it.w.flag_id});
-      else
-        written[key] = 1;
+      if (it.w.flags & kItemPartial) {
+        src_ptr[key + 1] += 1;
+        if (state[key] == 0) state[key] = 2;
+      } else {
+        state[key] = 1;
+      }
     }
   }
   if (composable) {
     // tokens a format lists must end up with a result even if no key covers them
     for (const BlockRow& r : rows)
       for (int32_t t = 0; t < r.qo_len; ++t)
-        for (int32_t h = 0; h < h_kv; ++h) needed[static_cast<size_t>(r.qo_begin + t) * h_kv + h] = 1;
+        for (int32_t h = 0; h < h_kv; ++h) {
+          const size_t key = static_cast<size_t>(r.qo_begin + t) * h_kv + h;
+          if (state[key] == 0) state[key] = 2;
+        }
+  }
+  for (size_t k = 0; k < nkeys; ++k) src_ptr[k + 1] += src_ptr[k];
+  if (nkeys == 0) src_ptr.assign(1, 0);
+  std::vector<MergeSrc> srcs(src_ptr[nkeys]);
+  {
+    std::vector<int32_t> fill(src_ptr.begin(), src_ptr.end() - 1);
+    for (const Item& it : items) {
+      if (!(it.w.flags & kItemPartial)) continue;
+      for (int32_t t = 0; t < it.w.qo_count; ++t) {
+        const size_t key = static_cast<size_t>(it.w.qo_begin + t) * h_kv + it.w.kv_head;
+        srcs[fill[key]++] = {it.w.partial_row + t * g, it.w.flag_id};
+      }
+    }
   }
   std::vector<MergeTask> tasks;
-  std::vector<MergeSrc> srcs;
-  for (size_t key = 0; key < srcs_of.size(); ++key) {
-    if (written[key]) continue;
-    if (srcs_of[key].empty() && !needed[key]) continue;
+  for (size_t key = 0; key < nkeys; ++key) {
+    if (state[key] != 2) continue;
     MergeTask m;
     m.qo_row = static_cast<int32_t>(key / h_kv);
     m.kv_head = static_cast<int32_t>(key % h_kv);
-    m.src_begin = static_cast<int32_t>(srcs.size());
-    m.src_count = static_cast<int32_t>(srcs_of[key].size());
-    srcs.insert(srcs.end(), srcs_of[key].begin(), srcs_of[key].end());
+    m.src_begin = src_ptr[key];
+    m.src_count = src_ptr[key + 1] - src_ptr[key];
     tasks.push_back(m);
   }
 
@@ -390,8 +412,11 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   }
 
   // ---- 3. maximum KV chunk (the pages' L_kv) and its refinements -------------
-  int64_t total_kv = 0;
-  for (const Unit& u : units) total_kv += u.l_eff;
+  int64_t total_kv = 0, max_leff = 0;
+  for (const Unit& u : units) {
+    total_kv += u.l_eff;
+    max_leff = std::max<int64_t>(max_leff, u.l_eff);
+  }
   const int64_t min_chunk = round_up(std::max(cfg.min_chunk, 1), kChunkGranule);
   const int64_t base_chunk =
       std::max<int64_t>(round_up(std::max<int64_t>(ceil_div(total_kv, nwg), 1), kChunkGranule), min_chunk);
@@ -401,8 +426,14 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   for (int k = 1; k <= kChunkCandidates + 1; ++k) {
     // candidates: the pages' L_kv, L_kv / k (k = 2..), then filling at L_kv
     const bool fill = k == kChunkCandidates + 1;
-    const int64_t chunk =
+    int64_t chunk =
         fill ? base_chunk : std::max<int64_t>(round_up(ceil_div(base_chunk, k), kChunkGranule), min_chunk);
+    // chunks at least as long as every unit cut nothing: all such candidates, and
+    // filling without long units, are the same plan
+    if (chunk >= max_leff) {
+      if (have) continue;
+      chunk = std::max<int64_t>(round_up(std::max<int64_t>(max_leff, 1), kChunkGranule), base_chunk);
+    }
     if (!fill && chunk == last_chunk) continue;
     last_chunk = chunk;
     Schedule cand;
