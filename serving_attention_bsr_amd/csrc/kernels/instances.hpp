@@ -34,19 +34,19 @@ inline void add_decode(std::vector<KernelEntry>* out) {
                   kDecodeWgPerCu});
 }
 
-// MFMA kernels: one workgroup per CU by default (the register and LDS use of the
-// MFMA body allow what the occupancy query reports).
-#ifndef BSR_MFMA_OCC
-#define BSR_MFMA_OCC 1
-#endif
-constexpr int kMfmaWgPerCu = BSR_MFMA_OCC;
+// MFMA kernels: two workgroups per CU for D <= 128, so that one workgroup's
+// softmax and gather run while the other's matrix products do (the body fits 256
+// registers per lane there); D = 256 holds a 128-float accumulator per lane and
+// runs one workgroup per CU.
+template <int D>
+constexpr int kMfmaOcc = D <= 128 ? 2 : 1;
 
 template <int D, bool CAP>
 inline void add_mfma(std::vector<KernelEntry>* out) {
   out->push_back({KernelKey{kKindMfma, true, D, 0, CAP},
                   reinterpret_cast<const void*>(
-                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, BSR_MFMA_OCC>),
-                  kMfmaWgPerCu});
+                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, kMfmaOcc<D>>),
+                  kMfmaOcc<D>});
 }
 
 template <int D, int ROWS, bool CAP>

@@ -11,17 +11,19 @@
 // gfx950 mapping.  A workgroup (4 wavefronts) owns 128 folded rows; wavefront w
 // owns rows 32w..32w+31.  Per tile of 64 keys:
 //   * the workgroup gathers the keys' K and V rows page by page (16-byte loads,
-//     one tile ahead, page ids two tiles ahead) and stages them in LDS: K row-major
-//     [key][D], V transposed [D][key] in the key order the P operand needs;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = the
+//     one tile ahead, page ids two tiles ahead) and stages both row-major in LDS,
+//     with the 16-byte chunks of each row XOR-swizzled by the row index so that
+//     the reads below hit distinct banks (no padding);
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //     wavefront's Q rows, held in registers for the whole item): each lane then
 //     holds one query column and 16 keys of each 32-key block, so the softmax max
 //     and sums are in-lane (plus one exchange between the two lane halves);
 //   * base-2 online softmax, soft-cap and the causal mask (only on tiles that
 //     cross the diagonal or the chunk end);
 //   * O^T += V^T P^T: the probabilities, converted to bf16, are the B operand in
-//     exactly the registers the S^T result left them in, because V^T is stored
-//     with its keys permuted to match; A = V^T from LDS.
+//     exactly the registers the S^T result left them in; the A operand V^T is read
+//     from the row-major V tile with the LDS transpose read (ds_read_b64_tr_b16),
+//     whose lane addresses follow the key order of the P registers.
 // The result leaves through the same emit callback as the decode body.
 #pragma once
 
@@ -32,6 +34,10 @@ namespace bsr {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
 template <int D, bool CAP>
 struct MfmaBody {
   static constexpr int BR = 128;           // folded rows per item
@@ -39,26 +45,25 @@ struct MfmaBody {
   static constexpr int KB = BC / 32;       // 32-key blocks per tile
   static constexpr int DK = D / 16;        // MFMA k-steps over D for S^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
-  static constexpr int KPAD = D + 8;       // K row stride in LDS (bf16)
-  static constexpr int VPAD = BC + 8;      // V^T row stride in LDS (bf16)
   static constexpr int NQ = BC / 4;        // key quads per tile
-  static constexpr int NCH = D / 8;        // 8-element chunks per row
+  static constexpr int NCH = D / 8;        // 16-byte chunks per row
   static constexpr int TASKS = NQ * NCH;   // (quad, chunk) load tasks per tile
   static constexpr int TPT = (TASKS + kWgThreads - 1) / kWgThreads;  // tasks per thread
-  static constexpr int LDS_BYTES = BC * KPAD * 2 + D * VPAD * 2;
+  static constexpr int LDS_BYTES = 2 * BC * D * 2;
   static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
 
-  // Position of key quad qd (0..BC/4) in the V^T row: within each 32-key block the
-  // k-index of the P operand is 16 s + 8 h + j, holding key quad 4 s + h + 2 (j/4).
-  static __device__ __forceinline__ int quad_pos(int qd) {
-    const int blk = qd >> 3, q = qd & 7;
-    return 32 * blk + 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
-  }
+  // Chunk swizzles (16-byte chunk index XOR a function of the key row).  K is read
+  // one row per lane, 16 lanes per pass: rows 0..15 must reach 16 distinct bank
+  // groups (a D=64 row covers half the banks, so row bit 0 picks the half).  V is
+  // read with the transpose read, 4 consecutive keys x 4 chunks per half-wave: the
+  // 4 rows must land on 4 distinct chunk groups.
+  static __device__ __forceinline__ int swz_k(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
 
   struct Loads {
-    uint4 k[TPT][4];
-    uint4 v[TPT][4];
+    u32x4_t k[TPT][4];
+    u32x4_t v[TPT][4];
   };
   struct Rows {
     uint32_t row[TPT][4];
@@ -100,13 +105,13 @@ struct MfmaBody {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint64_t off = static_cast<uint64_t>(rows.row[i][j]) * (D * 2) + ch * 16;
-        out.k[i][j] = *reinterpret_cast<const uint4*>(kb + off);
-        out.v[i][j] = *reinterpret_cast<const uint4*>(vb + off);
+        out.k[i][j] = *reinterpret_cast<const u32x4_t*>(kb + off);
+        out.v[i][j] = *reinterpret_cast<const u32x4_t*>(vb + off);
       }
     }
   }
 
-  // K row-major; V transposed with each key quad's four keys packed in 8 bytes.
+  // K and V row-major, chunks swizzled.
   static __device__ __forceinline__ void store_lds(const Loads& in, uint16_t* lk, uint16_t* lv) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -114,29 +119,23 @@ struct MfmaBody {
       task_of(i, qd, ch);
       if (TASKS % kWgThreads != 0 && qd >= NQ) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(lk + (4 * qd + j) * KPAD + 8 * ch) = in.k[i][j];
-      const int pos = quad_pos(qd);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t h[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = e < 2 ? in.v[i][j].x : e < 4 ? in.v[i][j].y : e < 6 ? in.v[i][j].z : in.v[i][j].w;
-          h[j] = (e & 1) ? (w >> 16) : (w & 0xffffu);
-        }
-        uint2 packed;
-        packed.x = h[0] | (h[1] << 16);
-        packed.y = h[2] | (h[3] << 16);
-        *reinterpret_cast<uint2*>(lv + (8 * ch + e) * VPAD + pos) = packed;
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * qd + j;
+        *reinterpret_cast<u32x4_t*>(lk + r * D + 8 * (ch ^ swz_k(r))) = in.k[i][j];
+        *reinterpret_cast<u32x4_t*>(lv + r * D + 8 * (ch ^ swz_v(r))) = in.v[i][j];
       }
     }
+  }
+
+  // Transpose read of 4 bf16 (one 8-byte half of a 16-byte chunk).
+  static __device__ __forceinline__ i16x4_t read_tr(const uint16_t* addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const_cast<uint16_t*>(addr)));
   }
 
   template <typename Emit>
   static __device__ void run(const RunParams& p, const WorkItem& it, float* lds_f, Emit&& emit) {
     uint16_t* lk = reinterpret_cast<uint16_t*>(lds_f);
-    uint16_t* lv = lk + BC * KPAD;
+    uint16_t* lv = lk + BC * D;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31;    // query column of this lane
@@ -154,8 +153,8 @@ struct MfmaBody {
       const int64_t qrow = static_cast<int64_t>(it.qo_begin + t_local) * p.h_qo + it.kv_head * g + rho % g;
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row_ok) v = *reinterpret_cast<const uint4*>(qb + qrow * D + 16 * ks + 8 * half);
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qb + qrow * D + 16 * ks + 8 * half);
         qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
@@ -194,8 +193,9 @@ struct MfmaBody {
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < DK; ++ks) {
+          const int r = 32 * kb + col;
           const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(lk + (32 * kb + col) * KPAD + 16 * ks + 8 * half));
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * D + 8 * ((2 * ks + half) ^ swz_k(r))));
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
         }
       }
@@ -246,17 +246,31 @@ struct MfmaBody {
           for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       }
 
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      // O^T += V^T P^T.  The P registers of step (kb, st) hold, in MFMA k order,
+      // keys 32 kb + 16 st + 4 half + {0..3} and then the same plus 8; the A
+      // operand lane (32 db + col, half) needs V^T at those keys.  With the transpose
+      // read, lane l of a 16-lane group receives element (l & 3) of the 4-element
+      // rows addressed by lanes 4 e + l / 4 (e = 0..3), so lane s addresses key
+      // base + s / 4 at d = 32 db + 16 (group & 1) + 4 (s & 3).
+      {
+        const int grp16 = lane >> 4, s16 = lane & 15;
+        const int key_off = 4 * (grp16 >> 1) + (s16 >> 2);
+        const int d_off = 16 * (grp16 & 1) + 4 * (s16 & 3);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const bf16x8_t a = __builtin_bit_cast(
-                bf16x8_t,
-                *reinterpret_cast<const uint4*>(lv + (32 * db + col) * VPAD + 32 * kb + 16 * st + 8 * half));
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][st], acc[db], 0, 0, 0);
+            const int r0 = 32 * kb + 16 * st + key_off;
+            const int r1 = r0 + 8;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int d = 32 * db + d_off;
+              const int c = d >> 3, e = d & 7;
+              const i16x4_t lo = read_tr(lv + r0 * D + 8 * (c ^ swz_v(r0)) + e);
+              const i16x4_t hi = read_tr(lv + r1 * D + 8 * (c ^ swz_v(r1)) + e);
+              const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][st], acc[db], 0, 0, 0);
+            }
           }
         }
       }
