@@ -11,9 +11,9 @@
 // gfx950 mapping.  A workgroup (4 wavefronts) owns 128 folded rows; wavefront w
 // owns rows 32w..32w+31.  Per tile of 64 keys:
 //   * the workgroup gathers the keys' K and V rows page by page (16-byte loads,
-//     one tile ahead, page ids two tiles ahead) and stages both row-major in LDS,
-//     with the 16-byte chunks of each row XOR-swizzled by the row index so that
-//     the reads below hit distinct banks (no padding);
+//     one tile ahead, page ids two tiles ahead) and stages both row-major in LDS;
+//     the row strides are padded so that the reads below hit distinct banks
+//     while every read address stays a per-lane base plus an immediate;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //     wavefront's Q rows, held in registers for the whole item): each lane then
 //     holds one query column and 16 keys of each 32-key block, so the softmax max
@@ -49,17 +49,16 @@ struct MfmaBody {
   static constexpr int NCH = D / 8;        // 16-byte chunks per row
   static constexpr int TASKS = NQ * NCH;   // (quad, chunk) load tasks per tile
   static constexpr int TPT = (TASKS + kWgThreads - 1) / kWgThreads;  // tasks per thread
-  static constexpr int LDS_BYTES = 2 * BC * D * 2;
+  // Row strides (bf16).  K is read one row per lane, 16 lanes per pass: a stride of
+  // D + 8 moves each row by 4 banks, so 16 rows fill the 64 banks.  V is read with
+  // the transpose read, 4 consecutive keys x 64 bytes per half-wave: a stride of
+  // 16 or 48 dwords modulo 64 puts the 4 rows on 4 distinct quarters of the banks.
+  static constexpr int KPAD = D + 8;
+  static constexpr int VPAD = D + 32;
+  static constexpr int LDS_BYTES = BC * (KPAD + VPAD) * 2;
   static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
 
-  // Chunk swizzles (16-byte chunk index XOR a function of the key row).  K is read
-  // one row per lane, 16 lanes per pass: rows 0..15 must reach 16 distinct bank
-  // groups (a D=64 row covers half the banks, so row bit 0 picks the half).  V is
-  // read with the transpose read, 4 consecutive keys x 4 chunks per half-wave: the
-  // 4 rows must land on 4 distinct chunk groups.
-  static __device__ __forceinline__ int swz_k(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
-  static __device__ __forceinline__ int swz_v(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
 
   struct Loads {
     u32x4_t k[TPT][4];
@@ -111,7 +110,7 @@ struct MfmaBody {
     }
   }
 
-  // K and V row-major, chunks swizzled.
+  // K and V row-major with padded strides.
   static __device__ __forceinline__ void store_lds(const Loads& in, uint16_t* lk, uint16_t* lv) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -121,8 +120,8 @@ struct MfmaBody {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * qd + j;
-        *reinterpret_cast<u32x4_t*>(lk + r * D + 8 * (ch ^ swz_k(r))) = in.k[i][j];
-        *reinterpret_cast<u32x4_t*>(lv + r * D + 8 * (ch ^ swz_v(r))) = in.v[i][j];
+        *reinterpret_cast<u32x4_t*>(lk + r * KPAD + 8 * ch) = in.k[i][j];
+        *reinterpret_cast<u32x4_t*>(lv + r * VPAD + 8 * ch) = in.v[i][j];
       }
     }
   }
@@ -135,7 +134,7 @@ struct MfmaBody {
   template <typename Emit>
   static __device__ void run(const RunParams& p, const WorkItem& it, float* lds_f, Emit&& emit) {
     uint16_t* lk = reinterpret_cast<uint16_t*>(lds_f);
-    uint16_t* lv = lk + BC * D;
+    uint16_t* lv = lk + BC * KPAD;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31;    // query column of this lane
@@ -165,6 +164,9 @@ struct MfmaBody {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
     float m_run = kNegInf;   // running max (base-2 units), shared by both lane halves
+    // logits in base 2 are c * s: without a soft-cap the scale is folded into the
+    // exponent's fma; with one, s is first mapped to cap * tanh(s / cap) in base 2
+    const float c = CAP ? 1.0f : p.scale_log2;
     float l_run = 0.0f;      // this half's share of the running sum
 
     const int ntok = it.kv_end - it.kv_begin;
@@ -195,34 +197,36 @@ struct MfmaBody {
         for (int ks = 0; ks < DK; ++ks) {
           const int r = 32 * kb + col;
           const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * D + 8 * ((2 * ks + half) ^ swz_k(r))));
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * KPAD + 16 * ks + 8 * half));
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
         }
       }
 
-      // logits in base 2, soft-cap, masks
+      // soft-cap, masks, tile maximum (of c * s, c > 0)
       const int tile_base = it.kv_begin + t * BC;
       const bool need_mask = tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit;
+      if constexpr (CAP) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = p.cap_log2 * tanh_exp(s[kb][r] * p.sm_scale * p.cap_inv);
+      }
+      if (need_mask) {
+        // key 32 kb + 8 (r / 4) + 4 half + r % 4 of the tile is visible up to the
+        // chunk end and this row's causal limit
+        const int lim = min(it.kv_end - 1, it.causal_limit + t_local) - tile_base - 4 * half;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = kNegInf;
+      }
       float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x;
-          if constexpr (CAP) {
-            x = p.cap_log2 * tanh_exp(s[kb][r] * p.sm_scale * p.cap_inv);
-          } else {
-            x = s[kb][r] * p.scale_log2;
-          }
-          if (need_mask) {
-            const int tau = tile_base + 32 * kb + (r >> 2) * 8 + 4 * half + (r & 3);
-            if (tau >= it.kv_end || tau > it.causal_limit + t_local) x = kNegInf;
-          }
-          s[kb][r] = x;
-          mx = __builtin_fmaxf(mx, x);
-        }
-      }
-      mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32));
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+      mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32)) * c;
       const float m_new = __builtin_fmaxf(m_run, mx);
       const float m_use = m_new == kNegInf ? 0.0f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
@@ -233,7 +237,7 @@ struct MfmaBody {
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(s[kb][r] - m_use);
+          const float e = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
           psum += e;
           pb[kb][r >> 3][r & 7] = static_cast<__bf16>(e);
         }
@@ -265,9 +269,8 @@ struct MfmaBody {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
               const int d = 32 * db + d_off;
-              const int c = d >> 3, e = d & 7;
-              const i16x4_t lo = read_tr(lv + r0 * D + 8 * (c ^ swz_v(r0)) + e);
-              const i16x4_t hi = read_tr(lv + r1 * D + 8 * (c ^ swz_v(r1)) + e);
+              const i16x4_t lo = read_tr(lv + r0 * VPAD + d);
+              const i16x4_t hi = read_tr(lv + r1 * VPAD + d);
               const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
               acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][st], acc[db], 0, 0, 0);
             }
