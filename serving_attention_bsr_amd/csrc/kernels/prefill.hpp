@@ -10,8 +10,9 @@
 //
 // gfx950 mapping.  A workgroup (4 wavefronts) owns 128 folded rows; wavefront w
 // owns rows 32w..32w+31.  Per tile of 64 keys:
-//   * the workgroup gathers the keys' K and V rows page by page (16-byte loads,
-//     one tile ahead, page ids two tiles ahead) and stages both row-major in LDS;
+//   * the workgroup gathers the keys' K and V rows page by page (16-byte loads
+//     into registers one tile ahead, page ids two tiles ahead) and stages both
+//     row-major in one of two LDS buffers, so that one barrier per tile suffices;
 //     the row strides are padded so that the reads below hit distinct banks
 //     while every read address stays a per-lane base plus an immediate;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
@@ -41,7 +42,7 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 template <int D, bool CAP>
 struct MfmaBody {
   static constexpr int BR = 128;           // folded rows per item
-  static constexpr int BC = 64;            // keys per tile
+  static constexpr int BC = D == 256 ? 32 : 64;  // keys per tile (fewer registers at D = 256)
   static constexpr int KB = BC / 32;       // 32-key blocks per tile
   static constexpr int DK = D / 16;        // MFMA k-steps over D for S^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -55,7 +56,8 @@ struct MfmaBody {
   // 16 or 48 dwords modulo 64 puts the 4 rows on 4 distinct quarters of the banks.
   static constexpr int KPAD = D + 8;
   static constexpr int VPAD = D + 32;
-  static constexpr int LDS_BYTES = BC * (KPAD + VPAD) * 2;
+  static constexpr int STAGE = BC * (KPAD + VPAD);   // bf16 elements of one buffer
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
 
@@ -131,10 +133,117 @@ struct MfmaBody {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const_cast<uint16_t*>(addr)));
   }
 
+  // ---- pieces of one tile step -------------------------------------------------
+
+  // S^T = K Q^T for the tile whose K rows start at lk (32-key blocks kb).
+  static __device__ __forceinline__ void qk(const uint16_t* lk, const bf16x8_t (&qreg)[DK], int col, int half,
+                                            f32x16_t (&s)[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const int r = 32 * kb + col;
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * KPAD + 16 * ks + 8 * half));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
+      }
+    }
+  }
+
+  // Soft-cap (base 2) and the chunk-end / causal mask of tile t.
+  static __device__ __forceinline__ void cap_and_mask(const RunParams& p, const WorkItem& it, int t, int t_local,
+                                                      int half, f32x16_t (&s)[KB]) {
+    if constexpr (CAP) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = p.cap_log2 * tanh_exp(s[kb][r] * p.sm_scale * p.cap_inv);
+    }
+    const int tile_base = it.kv_begin + t * BC;
+    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit) {
+      // key 32 kb + 8 (r / 4) + 4 half + r % 4 of the tile is visible up to the
+      // chunk end and this row's causal limit
+      asm volatile("");  // keep this a branch: only boundary tiles pay for the mask
+      const int lim = min(it.kv_end - 1, it.causal_limit + t_local) - tile_base - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = kNegInf;
+    }
+  }
+
+  // Online softmax of one tile: probabilities into the P registers (bf16), running
+  // max and sum updated; returns the factor the accumulator must be scaled by.
+  static __device__ __forceinline__ float softmax(const f32x16_t (&s)[KB], float c, float& m_run, float& l_run,
+                                                  bf16x8_t (&pb)[KB][2]) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32)) * c;
+    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+        psum += e;
+        pb[kb][r >> 3][r & 7] = static_cast<__bf16>(e);
+      }
+    }
+    l_run = l_run * alpha + psum;
+    return alpha;
+  }
+
+  static __device__ __forceinline__ void rescale(float alpha, f32x16_t (&acc)[DB]) {
+    if (__ballot(alpha != 1.0f) != 0) {
+      // a real branch (the empty asm keeps the compiler from predicating the
+      // rescale into every tile): most tiles leave the running maxima unchanged
+      asm volatile("");
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+  }
+
+  // O^T += V^T P^T.  The P registers of step (kb, st) hold, in MFMA k order, keys
+  // 32 kb + 16 st + 4 half + {0..3} and then the same plus 8; the A operand lane
+  // (32 db + col, half) needs V^T at those keys.  With the transpose read, lane l
+  // of a 16-lane group receives element (l & 3) of the 4-element rows addressed
+  // by lanes 4 e + l / 4 (e = 0..3), so lane s addresses key base + s / 4 at
+  // d = 32 db + 16 (group & 1) + 4 (s & 3): key_off and d_off below.
+  static __device__ __forceinline__ void pv(const uint16_t* lv, const bf16x8_t (&pb)[KB][2], int key_off,
+                                            int d_off, f32x16_t (&acc)[DB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int r0 = 32 * kb + 16 * st + key_off;
+        const int r1 = r0 + 8;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int d = 32 * db + d_off;
+          const i16x4_t lo = read_tr(lv + r0 * VPAD + d);
+          const i16x4_t hi = read_tr(lv + r1 * VPAD + d);
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][st], acc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
   template <typename Emit>
   static __device__ void run(const RunParams& p, const WorkItem& it, float* lds_f, Emit&& emit) {
-    uint16_t* lk = reinterpret_cast<uint16_t*>(lds_f);
-    uint16_t* lv = lk + BC * KPAD;
+    uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_f);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31;    // query column of this lane
@@ -144,6 +253,8 @@ struct MfmaBody {
     const int rho = wave * 32 + col;                  // folded row of this lane's column
     const bool row_ok = rho < rows_valid;
     const int t_local = rho / g;
+    const int key_off = 4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2);
+    const int d_off = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     // Q rows of this wavefront as the B operand: Q[rho][16 ks + 8 half + 0..7]
     bf16x8_t qreg[DK];
@@ -173,110 +284,38 @@ struct MfmaBody {
     const int ntiles = (ntok + BC - 1) / BC;
     Rows rows_next;
     Loads regs;
+    // Two buffers: tile t lives in buffer t % 2; the registers carry tile t + 1
+    // while tile t is computed and go to the other buffer at the next step.
     if (ntiles > 0) {
       load_rows(p, it, 0, rows_next);
       load_kv(p, rows_next, regs);
-      load_rows(p, it, 1 < ntiles ? 1 : 0, rows_next);
+      store_lds(regs, lds_h, lds_h + BC * KPAD);
+      if (ntiles > 1) {
+        load_rows(p, it, 1, rows_next);
+        load_kv(p, rows_next, regs);
+        load_rows(p, it, ntiles > 2 ? 2 : 1, rows_next);
+      }
     }
     for (int t = 0; t < ntiles; ++t) {
-      __syncthreads();  // every wavefront is done reading the previous tile
-      store_lds(regs, lk, lv);
-      if (t + 1 < ntiles) {
-        load_kv(p, rows_next, regs);
-        load_rows(p, it, t + 2 < ntiles ? t + 2 : t + 1, rows_next);
-      }
+      // tile t is in its buffer; every wavefront is done with tile t - 1, whose
+      // buffer now takes tile t + 1
       __syncthreads();
-
-      // S^T = K Q^T, two 32-key blocks
+      const uint16_t* lk = lds_h + (t & 1) * STAGE;
+      if (t + 1 < ntiles) {
+        uint16_t* nk = lds_h + ((t + 1) & 1) * STAGE;
+        store_lds(regs, nk, nk + BC * KPAD);
+        if (t + 2 < ntiles) {
+          load_kv(p, rows_next, regs);
+          load_rows(p, it, t + 3 < ntiles ? t + 3 : t + 2, rows_next);
+        }
+      }
       f32x16_t s[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-          const int r = 32 * kb + col;
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * KPAD + 16 * ks + 8 * half));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
-        }
-      }
-
-      // soft-cap, masks, tile maximum (of c * s, c > 0)
-      const int tile_base = it.kv_begin + t * BC;
-      const bool need_mask = tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit;
-      if constexpr (CAP) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][r] = p.cap_log2 * tanh_exp(s[kb][r] * p.sm_scale * p.cap_inv);
-      }
-      if (need_mask) {
-        // key 32 kb + 8 (r / 4) + 4 half + r % 4 of the tile is visible up to the
-        // chunk end and this row's causal limit
-        const int lim = min(it.kv_end - 1, it.causal_limit + t_local) - tile_base - 4 * half;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = kNegInf;
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
-      mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32)) * c;
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.0f;
+      qk(lk, qreg, col, half, s);
+      cap_and_mask(p, it, t, t_local, half, s);
       bf16x8_t pb[KB][2];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-          psum += e;
-          pb[kb][r >> 3][r & 7] = static_cast<__bf16>(e);
-        }
-      }
-      l_run = l_run * alpha + psum;
-      if (__ballot(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      }
-
-      // O^T += V^T P^T.  The P registers of step (kb, st) hold, in MFMA k order,
-      // keys 32 kb + 16 st + 4 half + {0..3} and then the same plus 8; the A
-      // operand lane (32 db + col, half) needs V^T at those keys.  With the transpose
-      // read, lane l of a 16-lane group receives element (l & 3) of the 4-element
-      // rows addressed by lanes 4 e + l / 4 (e = 0..3), so lane s addresses key
-      // base + s / 4 at d = 32 db + 16 (group & 1) + 4 (s & 3).
-      {
-        const int grp16 = lane >> 4, s16 = lane & 15;
-        const int key_off = 4 * (grp16 >> 1) + (s16 >> 2);
-        const int d_off = 16 * (grp16 & 1) + 4 * (s16 & 3);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const int r0 = 32 * kb + 16 * st + key_off;
-            const int r1 = r0 + 8;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const int d = 32 * db + d_off;
-              const i16x4_t lo = read_tr(lv + r0 * VPAD + d);
-              const i16x4_t hi = read_tr(lv + r1 * VPAD + d);
-              const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][st], acc[db], 0, 0, 0);
-            }
-          }
-        }
-      }
+      const float alpha = softmax(s, c, m_run, l_run, pb);
+      rescale(alpha, acc);
+      pv(lk + BC * KPAD, pb, key_off, d_off, acc);
     }
 
     // result: this lane's column holds O^T[d][rho] for d = 32 db + 8 (r/4) + 4 half + r%4
