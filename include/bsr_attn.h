@@ -105,7 +105,11 @@ typedef struct bsr_attn_config {
   int32_t max_partial_rows;/* partial-state capacity in folded rows; 0 = derived bound */
   int32_t cost_item;       /* fixed cost of one work item, in KV-token units (pipeline
                               fill and drain); 0 selects the default, < 0 selects none */
-  int32_t reserved[2];     /* must be 0 */
+  int32_t cost_mfma;       /* cost of one KV token of an MFMA (tile) work item relative
+                              to one of a decode work item, in sixteenths; used when one
+                              grid runs both bodies (composed formats, mixed batches);
+                              0 selects the measured default for the head dim */
+  int32_t reserved[1];     /* must be 0 */
 } bsr_attn_config;
 
 /* One BSR sub-matrix for bsr_attn_plan_composable().  Arrays are host memory. */

@@ -122,8 +122,9 @@ int validate_config(const bsr_attn_config* c) {
     return fail(BSR_ERR_INVALID_ARG, "max_batch, max_total_qo and max_total_kv must be positive");
   if (c->max_total_kv >= (int64_t(1) << 40)) return fail(BSR_ERR_INVALID_ARG, "max_total_kv too large");
   if (c->num_workgroups < 0 || c->cost_alpha < 0 || c->cost_beta < 0 || c->min_kv_chunk < 0 ||
-      c->max_partial_rows < 0)
+      c->max_partial_rows < 0 || c->cost_mfma < 0)
     return fail(BSR_ERR_INVALID_ARG, "negative tuning parameter");
+  if (c->cost_mfma > 16 * 256) return fail(BSR_ERR_INVALID_ARG, "cost_mfma too large");
   for (int32_t r : c->reserved)
     if (r != 0) return fail(BSR_ERR_INVALID_ARG, "reserved fields must be zero");
   return BSR_OK;
@@ -227,6 +228,10 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.beta = cfg->cost_beta > 0 ? cfg->cost_beta : 1;
   pc.min_chunk = cfg->min_kv_chunk > 0 ? cfg->min_kv_chunk : 64;
   pc.gamma = cfg->cost_item > 0 ? cfg->cost_item : (cfg->cost_item < 0 ? 0 : 512);
+  // Default from a sweep on MI355X (shared-prefix batches, D = 64, 128, 256): the
+  // mixed grid runs fastest once MFMA pieces get workgroups of their own, which
+  // every weight from 10x up gives; 12x is used.
+  pc.mfma_w16 = cfg->cost_mfma > 0 ? cfg->cost_mfma : 192;
   pc.max_batch = cfg->max_batch;
   pc.max_total_qo = cfg->max_total_qo;
   pc.max_total_kv = cfg->max_total_kv;

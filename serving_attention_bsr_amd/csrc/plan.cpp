@@ -14,7 +14,10 @@
 //   4. units longer than L_kv are cut into equal chunks of at most L_kv; only
 //      those write partial states, the rest write O/LSE directly;
 //   5. cost = alpha * rows + beta * KV tokens (+ gamma, a fixed per-item cost
-//      that models pipeline fill and drain; an extension of the pages' model);
+//      that models pipeline fill and drain; an extension of the pages' model;
+//      when one grid runs both bodies, an MFMA unit's tokens are weighted by the
+//      measured ratio of the two bodies' time per token, and L_kv is counted in
+//      weighted tokens);
 //      items sorted by cost, longest first, each given to the least-loaded
 //      workgroup (min-heap on (load, workgroup id)), so the plan depends on the
 //      lengths only;
@@ -51,7 +54,15 @@ struct Unit {
   int32_t l_eff;
   int32_t causal_limit;
   bool mfma;
+  int32_t w16;  // cost of one KV token in sixteenths (16 except MFMA units of a mixed grid)
 };
+
+// KV tokens weighted by the unit's token cost.
+inline int64_t weighted(const Unit& u, int64_t keys) { return (keys * u.w16 + 15) / 16; }
+// Longest piece of a unit that stays within `chunk` weighted tokens.
+inline int64_t unit_chunk(const Unit& u, int64_t chunk) {
+  return std::max<int64_t>(kChunkGranule, chunk * 16 / u.w16 / kChunkGranule * kChunkGranule);
+}
 
 struct Item {
   WorkItem w;
@@ -126,7 +137,7 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
     return w;
   };
   auto item_cost = [&](int32_t ui, int64_t keys) {
-    return cfg.alpha * static_cast<int64_t>(units[ui].nt) * g + cfg.beta * keys + cfg.gamma;
+    return cfg.alpha * static_cast<int64_t>(units[ui].nt) * g + cfg.beta * weighted(units[ui], keys) + cfg.gamma;
   };
 
   // ---- 4. chunks -> items, and 7a. their assignment --------------------------
@@ -143,7 +154,7 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
         items.push_back({w, item_cost(ui, 0), ui, 1});
         continue;
       }
-      const int64_t n = ceil_div(u.l_eff, chunk);
+      const int64_t n = ceil_div(u.l_eff, unit_chunk(u, chunk));
       const int64_t csz = n == 1 ? u.l_eff : round_up(ceil_div(u.l_eff, n), kChunkGranule);
       for (int64_t b = 0; b < u.l_eff; b += csz) {
         w.kv_begin = static_cast<int32_t>(b);
@@ -160,12 +171,14 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
     for (int32_t ui = 0; ui < static_cast<int32_t>(units.size()); ++ui) {
       const Unit& u = units[ui];
       if (u.l_eff == 0 && composable) continue;
-      (u.l_eff <= chunk ? short_u : long_u).push_back(ui);
+      (u.l_eff <= unit_chunk(u, chunk) ? short_u : long_u).push_back(ui);
       total += item_cost(ui, u.l_eff);
     }
     // filling cuts about one piece per workgroup beyond one per long unit
     if (!long_u.empty()) total += cfg.gamma * nwg;
-    auto longer = [&](int32_t a, int32_t b) { return units[a].l_eff > units[b].l_eff; };
+    auto longer = [&](int32_t a, int32_t b) {
+      return weighted(units[a], units[a].l_eff) > weighted(units[b], units[b].l_eff);
+    };
     std::stable_sort(short_u.begin(), short_u.end(), longer);
     std::stable_sort(long_u.begin(), long_u.end(), longer);
     const int64_t target = ceil_div(total, nwg);
@@ -193,13 +206,15 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
       while (pos < len) {
         const int64_t rem = len - pos;
         const int64_t fixed = item_cost(ui, 0);
-        const int64_t space = target - heap.top().first - fixed;
+        // room left in the least-loaded workgroup, in this unit's KV tokens
+        const int64_t space =
+            (target - heap.top().first - fixed) * 16 / (static_cast<int64_t>(units[ui].w16) * std::max<int64_t>(cfg.beta, 1));
         // pieces round up to the granule (the rounding overshoot is absorbed by
         // workgroups that end up with no long piece) and are never tiny
         const int64_t floor_piece = std::max<int64_t>(min_piece, 4 * kChunkGranule);
         // and at most twice L_kv (the fixed item cost makes a full workgroup hold
         // a little more than L_kv keys)
-        const int64_t cap = 2 * chunk;
+        const int64_t cap = 2 * unit_chunk(units[ui], chunk);
         int64_t piece = std::min(rem, cap);
         if (piece > space) {
           piece = std::min(cap, std::max(floor_piece, round_up(std::max<int64_t>(space, 0), kChunkGranule)));
@@ -307,8 +322,11 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
     out->makespan = std::max(out->makespan, l);
     out->total += l;
   }
-  // the longest chunk actually cut (L_kv for the pages' rule; filling may cut more)
-  out->chunk = chunk;
+  // the longest chunk actually cut (L_kv for the pages' rule; filling may cut more;
+  // with weighted units L_kv is not in tokens, so only the pieces count)
+  bool weighted_units = false;
+  for (const Unit& u : units) weighted_units |= u.w16 != 16;
+  out->chunk = weighted_units ? 0 : chunk;
   for (const Item& it : items)
     if (it.nchunks > 1) out->chunk = std::max<int64_t>(out->chunk, it.w.kv_end - it.w.kv_begin);
   out->partial_rows = partial_rows;
@@ -399,6 +417,9 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
         u.t0 = t0;
         u.nt = std::min(tile_tokens, r.qo_len - t0);
         u.mfma = mfma;
+        // the two bodies differ in time per KV token; only a grid that runs both
+        // needs the weight (single-body plans keep the pages' key counts)
+        u.w16 = kernel == kKindMixed && mfma ? std::max(cfg.mfma_w16, 1) : 16;
         if (cfg.causal) {
           u.causal_limit = r.kv_len - r.qo_len + t0;
           u.l_eff = std::min<int32_t>(r.kv_len, u.causal_limit + u.nt);
@@ -412,10 +433,11 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   }
 
   // ---- 3. maximum KV chunk (the pages' L_kv) and its refinements -------------
+  // (in weighted KV tokens: plain tokens unless a mixed grid weights MFMA units)
   int64_t total_kv = 0, max_leff = 0;
   for (const Unit& u : units) {
-    total_kv += u.l_eff;
-    max_leff = std::max<int64_t>(max_leff, u.l_eff);
+    total_kv += weighted(u, u.l_eff);
+    max_leff = std::max<int64_t>(max_leff, weighted(u, u.l_eff));
   }
   const int64_t min_chunk = round_up(std::max(cfg.min_chunk, 1), kChunkGranule);
   const int64_t base_chunk =

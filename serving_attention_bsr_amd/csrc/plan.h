@@ -24,6 +24,9 @@ struct PlanConfig {
   int64_t alpha = 1, beta = 1;
   int64_t gamma = 512;       // fixed cost of a work item or merge task (KV-token units)
   int32_t min_chunk = 64;
+  // cost of one KV token of an MFMA item in a mixed grid, in sixteenths of a
+  // decode item's token (16 = equal)
+  int32_t mfma_w16 = 16;
   // capacities (plan rejected beyond them)
   int32_t max_batch = 0, max_total_qo = 0;
   int64_t max_total_kv = 0;

@@ -71,7 +71,8 @@ class bsr_attn_config(ctypes.Structure):
         ("min_kv_chunk", ctypes.c_int32),
         ("max_partial_rows", ctypes.c_int32),
         ("cost_item", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("cost_mfma", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
 
@@ -258,6 +259,7 @@ class BsrAttention:
         min_kv_chunk: int = 0,
         max_partial_rows: int = 0,
         cost_item: int = 0,
+        cost_mfma: int = 0,
     ):
         cfg = bsr_attn_config()
         cfg.num_qo_heads = num_qo_heads
@@ -277,6 +279,7 @@ class BsrAttention:
         cfg.min_kv_chunk = min_kv_chunk
         cfg.max_partial_rows = max_partial_rows
         cfg.cost_item = cost_item
+        cfg.cost_mfma = cost_mfma
         self.cfg = cfg
         self.dtype = dtype
         self.device = device

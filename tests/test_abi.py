@@ -31,7 +31,7 @@ def test_abi_version():
 
 
 def test_struct_sizes_match_header():
-    # bsr_attn_config: 8 int32/float, max_batch, max_total_qo, int64, 5 int32, reserved[3]
+    # bsr_attn_config: 8 int32/float, max_batch, max_total_qo, int64, 7 int32, reserved[1]
     assert lib.ctypes.sizeof(lib.bsr_attn_config) == 80
     assert lib.ctypes.sizeof(lib.bsr_plan_info) == 64
 
@@ -58,3 +58,11 @@ def test_create_rejects_bad_config(kw, code):
     with pytest.raises(lib.BsrError) as e:
         lib.BsrAttention(**args)
     assert e.value.code == code
+
+
+def test_create_rejects_bad_cost_mfma():
+    for bad in (-1, 16 * 256 + 1):
+        with pytest.raises(lib.BsrError) as e:
+            lib.BsrAttention(8, 2, 64, 16, num_workgroups=4, device=-1, max_batch=4, max_total_qo=4,
+                             max_total_kv=64, cost_mfma=bad)
+        assert e.value.code == lib.BSR_ERR_INVALID_ARG

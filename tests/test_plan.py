@@ -80,12 +80,13 @@ def test_plan_splits_and_merges_when_work_is_long():
     assert np.all(plan["items"]["kv_end"][partial] - plan["items"]["kv_begin"][partial] <= info["kv_chunk"])
 
 
-def test_composable_plan_executes_to_oracle():
+@pytest.mark.parametrize("cost_mfma", [0, 16, 400])
+def test_composable_plan_executes_to_oracle(cost_mfma):
     w = W.shared_prefix_composable(
         seed=9, branches=6, prefix_len=48, suf_lo=1, suf_hi=40, page_size=16, num_qo_heads=8, num_kv_heads=2,
         head_dim=64,
     )
-    h = host_handle(8, 2, 64, 16, nwg=6)
+    h = host_handle(8, 2, 64, 16, nwg=6, cost_mfma=cost_mfma)
     fm = [f.as_dict() for f in w.formats]
     info = h.plan_composable(fm, w.batch)
     assert info["kernel"] == lib.KERNEL_MIXED
@@ -96,6 +97,42 @@ def test_composable_plan_executes_to_oracle():
     assert np.all(written == 1)
     np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-12)
+
+
+def test_mixed_grid_weights_mfma_tokens():
+    """In a grid that runs both bodies, an MFMA unit's KV tokens cost cost_mfma/16
+    decode tokens: a heavier weight cuts the shared prefix into more, shorter
+    pieces, and at the default the prefix work is spread over every workgroup
+    (each holds the same number of MFMA pieces, give or take one).  Plans with one
+    body do not depend on the weight."""
+    w = W.shared_prefix_composable(tensors=False)
+    fm = [f.as_dict() for f in w.formats]
+    mb = w.batch + sum(len(f.qo_indptr) - 1 for f in w.formats)
+
+    def plan(cost_mfma):
+        h = host_handle(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, nwg=256, max_batch=mb,
+                        cost_mfma=cost_mfma)
+        info = h.plan_composable(fm, w.batch)
+        return info, plan_blob.decode(h.plan_bytes())
+
+    light_info, light = plan(16)
+    heavy_info, heavy = plan(0)
+    mf = lambda p: p["items"][(p["items"]["flags"] & plan_blob.ITEM_MFMA) != 0]
+    assert len(mf(heavy)) > len(mf(light))
+    lens = lambda p: mf(p)["kv_end"] - mf(p)["kv_begin"]
+    assert lens(heavy).max() < lens(light).max()
+    ptr = heavy["item_ptr"]
+    nwg = heavy["header"]["num_wg"]
+    per_wg = [int(((heavy["items"][ptr[i]:ptr[i + 1]]["flags"] & plan_blob.ITEM_MFMA) != 0).sum()) for i in range(nwg)]
+    assert len(mf(heavy)) >= nwg
+    assert max(per_wg) - min(per_wg) <= 1
+    d = W.batch_decode(tensors=False)
+    bytes_for = []
+    for cm in (16, 400):
+        h = host_handle(d.num_qo_heads, d.num_kv_heads, d.head_dim, d.page_size, nwg=256, cost_mfma=cm)
+        h.plan(d.qo_indptr, d.kv_indptr, d.last_page_len)
+        bytes_for.append(h.plan_bytes().tobytes())
+    assert bytes_for[0] == bytes_for[1]
 
 
 def unit_chunks(plan, group):
