@@ -32,6 +32,8 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <climits>
+#include <cstdint>
 #include <cstring>
 #include <functional>
 #include <queue>
@@ -100,6 +102,7 @@ struct Schedule {
   std::vector<MergeTask> tasks;
   std::vector<MergeSrc> srcs;
   std::vector<int32_t> owner, order, mowner, morder;
+  std::vector<int64_t> att_load;  // attention cost per workgroup
   int64_t partial_rows = 0;
   int32_t num_flags = 0, num_partial_items = 0;
   int64_t makespan = 0, total = 0;
@@ -311,10 +314,13 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
   }
 
   // ---- 7b. merge tasks, longest first, on top of the attention loads ---------
+  // (a quick estimate to compare candidates; the chosen plan's tasks are then
+  // placed with their ready times, see assign_merges)
   std::vector<int64_t> mcosts(tasks.size());
   for (size_t i = 0; i < tasks.size(); ++i)
     mcosts[i] = cfg.gamma + cfg.beta * static_cast<int64_t>(tasks[i].src_count) * g;
   std::vector<int32_t> mowner, morder;
+  out->att_load = load;
   assign_longest_first(mcosts, &load, &mowner, &morder);
   out->makespan = 0;
   out->total = 0;
@@ -344,6 +350,71 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
 }
 
 }  // namespace
+
+// Merge tasks of the chosen schedule.  A task can start only when every
+// workgroup holding one of its sources has finished its attention items (its
+// release follows all of them), and a workgroup merges after its own attention
+// and after the sources of all its tasks are ready.  Tasks go longest first to the
+// workgroup where they would finish first, so tasks that become ready together at
+// the end of the attention phase are spread instead of stacked on the
+// least-loaded workgroups.  A workgroup without tasks whose attention ends by the
+// task's ready time is always a best choice; among those the least loaded (then
+// lowest id) is taken.
+static void assign_merges(const PlanConfig& cfg, int32_t nwg, Schedule* s) {
+  const int32_t g = cfg.group;
+  const size_t nt = s->tasks.size();
+  std::vector<int64_t> mcosts(nt);
+  for (size_t i = 0; i < nt; ++i)
+    mcosts[i] = cfg.gamma + cfg.beta * static_cast<int64_t>(s->tasks[i].src_count) * g;
+  std::vector<int64_t> flag_ready(s->num_flags, 0);
+  for (size_t i = 0; i < s->items.size(); ++i)
+    if (s->items[i].w.flag_id >= 0) flag_ready[s->items[i].w.flag_id] = s->att_load[s->owner[i]];
+  std::vector<int64_t> ready(nt, 0);
+  for (size_t i = 0; i < nt; ++i)
+    for (int32_t k = 0; k < s->tasks[i].src_count; ++k)
+      ready[i] = std::max(ready[i], flag_ready[s->srcs[s->tasks[i].src_begin + k].flag_id]);
+  s->morder.resize(nt);
+  for (size_t i = 0; i < nt; ++i) s->morder[i] = static_cast<int32_t>(i);
+  std::stable_sort(s->morder.begin(), s->morder.end(), [&](int32_t a, int32_t b) { return mcosts[a] > mcosts[b]; });
+  s->mowner.assign(nt, -1);
+  const std::vector<int64_t>& att = s->att_load;
+  std::vector<int64_t> mready(nwg, 0), msum(nwg, 0);
+  std::vector<int32_t> busy;  // workgroups holding tasks
+  using Slot = std::pair<int64_t, int32_t>;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> idle;  // (attention load, wg)
+  for (int32_t w = 0; w < nwg; ++w) idle.push({att[w], w});
+  for (int32_t i : s->morder) {
+    int32_t best_w = -1;
+    int64_t best_f = INT64_MAX;
+    if (!idle.empty()) {
+      best_w = idle.top().second;
+      best_f = std::max(att[best_w], ready[i]) + mcosts[i];
+    }
+    if (idle.empty() || att[best_w] > ready[i]) {
+      for (int32_t w : busy) {
+        const int64_t f = std::max(att[w], std::max(mready[w], ready[i])) + msum[w] + mcosts[i];
+        if (f < best_f || (f == best_f && w < best_w)) {
+          best_f = f;
+          best_w = w;
+        }
+      }
+    }
+    if (msum[best_w] == 0) {
+      idle.pop();  // best_w was the idle top (busy workgroups have msum > 0)
+      busy.push_back(best_w);
+    }
+    s->mowner[i] = best_w;
+    mready[best_w] = std::max(mready[best_w], ready[i]);
+    msum[best_w] += mcosts[i];
+  }
+  s->makespan = 0;
+  s->total = 0;
+  for (int32_t w = 0; w < nwg; ++w) {
+    const int64_t l = msum[w] > 0 ? std::max(att[w], mready[w]) + msum[w] : att[w];
+    s->makespan = std::max(s->makespan, l);
+    s->total += l;
+  }
+}
 
 int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t total_qo,
               bool composable, PlanResult* out, std::string* err) {
@@ -466,6 +537,7 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       have = true;
     }
   }
+  assign_merges(cfg, nwg, &best);
   if (best.partial_rows > cfg.max_partial_rows) {
     *err = "plan needs " + std::to_string(best.partial_rows) + " partial rows, capacity is " +
            std::to_string(cfg.max_partial_rows);
