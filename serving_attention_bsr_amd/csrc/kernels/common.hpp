@@ -42,6 +42,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Row gather through a structured buffer resource: the address unit computes
+// base + row * stride + offset itself, so a KV row index (32 bits, pools up to
+// 2^31 rows) needs no 64-bit address arithmetic on the vector ALU.  Offsets stay
+// below the row stride (the range check of structured buffers).
+__device__ u32x4_t bsr_struct_load_b128(__amdgpu_buffer_rsrc_t rsrc, int vindex, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
+
+// Element i of a 32-bit array through a raw buffer resource (32-bit offset).
+__device__ __forceinline__ uint32_t load_u32(__amdgpu_buffer_rsrc_t rsrc, int i) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rsrc, i * 4, 0, 0);
+}
+
+// Resource over rows of `stride` bytes starting at base (dword 3: 32-bit data,
+// the raw-buffer format of gfx9 parts).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int stride) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(stride), 0x7fffffff,
+                                           0x00020000);
+}
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);

@@ -36,7 +36,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 template <int D, bool CAP>
@@ -76,8 +75,8 @@ struct MfmaBody {
     ch = task % NCH;
   }
 
-  static __device__ __forceinline__ void load_rows(const RunParams& p, const WorkItem& it, int tile,
-                                                   Rows& out) {
+  static __device__ __forceinline__ void load_rows(const RunParams& p, __amdgpu_buffer_rsrc_t ir,
+                                                   const WorkItem& it, int tile, Rows& out) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       int qd, ch;
@@ -88,16 +87,16 @@ struct MfmaBody {
         tau = min(tau, it.kv_end - 1);
         const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
         const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-        const uint32_t page = static_cast<uint32_t>(p.kv_indices[it.page_begin + static_cast<int32_t>(pl)]);
-        out.row[i][j] = (page * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head)) *
-                            static_cast<uint32_t>(p.page_size) + slot;
+        const uint32_t page = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+        // (page * H_kv + head) * P + slot
+        out.row[i][j] = page * static_cast<uint32_t>(p.h_kv * p.page_size) +
+                        (static_cast<uint32_t>(it.kv_head * p.page_size) + slot);
       }
     }
   }
 
-  static __device__ __forceinline__ void load_kv(const RunParams& p, const Rows& rows, Loads& out) {
-    const uint8_t* kb = static_cast<const uint8_t*>(p.k_pool);
-    const uint8_t* vb = static_cast<const uint8_t*>(p.v_pool);
+  static __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                                 const Rows& rows, Loads& out) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       int qd, ch;
@@ -105,9 +104,9 @@ struct MfmaBody {
       if (TASKS % kWgThreads != 0 && qd >= NQ) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint64_t off = static_cast<uint64_t>(rows.row[i][j]) * (D * 2) + ch * 16;
-        out.k[i][j] = *reinterpret_cast<const u32x4_t*>(kb + off);
-        out.v[i][j] = *reinterpret_cast<const u32x4_t*>(vb + off);
+        const int row = static_cast<int>(rows.row[i][j]);
+        out.k[i][j] = bsr_struct_load_b128(kr, row, ch * 16, 0, 0);
+        out.v[i][j] = bsr_struct_load_b128(vr, row, ch * 16, 0, 0);
       }
     }
   }
@@ -282,18 +281,21 @@ struct MfmaBody {
 
     const int ntok = it.kv_end - it.kv_begin;
     const int ntiles = (ntok + BC - 1) / BC;
+    const __amdgpu_buffer_rsrc_t krs = row_rsrc(p.k_pool, D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, D * 2);
+    const __amdgpu_buffer_rsrc_t irs = row_rsrc(p.kv_indices, 0);
     Rows rows_next;
     Loads regs;
     // Two buffers: tile t lives in buffer t % 2; the registers carry tile t + 1
     // while tile t is computed and go to the other buffer at the next step.
     if (ntiles > 0) {
-      load_rows(p, it, 0, rows_next);
-      load_kv(p, rows_next, regs);
+      load_rows(p, irs, it, 0, rows_next);
+      load_kv(krs, vrs, rows_next, regs);
       store_lds(regs, lds_h, lds_h + BC * KPAD);
       if (ntiles > 1) {
-        load_rows(p, it, 1, rows_next);
-        load_kv(p, rows_next, regs);
-        load_rows(p, it, ntiles > 2 ? 2 : 1, rows_next);
+        load_rows(p, irs, it, 1, rows_next);
+        load_kv(krs, vrs, rows_next, regs);
+        load_rows(p, irs, it, ntiles > 2 ? 2 : 1, rows_next);
       }
     }
     for (int t = 0; t < ntiles; ++t) {
@@ -305,8 +307,8 @@ struct MfmaBody {
         uint16_t* nk = lds_h + ((t + 1) & 1) * STAGE;
         store_lds(regs, nk, nk + BC * KPAD);
         if (t + 2 < ntiles) {
-          load_kv(p, rows_next, regs);
-          load_rows(p, it, t + 3 < ntiles ? t + 3 : t + 2, rows_next);
+          load_kv(krs, vrs, rows_next, regs);
+          load_rows(p, irs, it, t + 3 < ntiles ? t + 3 : t + 2, rows_next);
         }
       }
       f32x16_t s[KB];
