@@ -53,31 +53,31 @@ struct DecodeBody {
     return (j / EPL) * (LPT * EPL) + c * EPL + (j % EPL);
   }
 
-  static __device__ __forceinline__ void load_pids(const RunParams& p, const WorkItem& it,
-                                                   int tile, int grp, Pids& out) {
+  static __device__ __forceinline__ void load_pids(const RunParams& p, __amdgpu_buffer_rsrc_t ir,
+                                                   const WorkItem& it, int tile, int grp, Pids& out) {
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
       int tau = it.kv_begin + tile * TILE + i * NG + grp;
       tau = min(tau, it.kv_end - 1);
       const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
       const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-      const uint32_t page = static_cast<uint32_t>(p.kv_indices[it.page_begin + static_cast<int32_t>(pl)]);
-      out.row[i] = (page * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head)) *
-                       static_cast<uint32_t>(p.page_size) + slot;
+      const uint32_t page = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+      // (page * H_kv + head) * P + slot
+      out.row[i] = page * static_cast<uint32_t>(p.h_kv * p.page_size) +
+                   (static_cast<uint32_t>(it.kv_head * p.page_size) + slot);
     }
   }
 
-  static __device__ __forceinline__ void load_kv(const RunParams& p, const WorkItem& it, int c,
+  // K/V rows through structured buffer resources over rows of D elements.
+  static __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int c,
                                                  const Pids& ids, Kv& out) {
-    const uint8_t* kb = static_cast<const uint8_t*>(p.k_pool);
-    const uint8_t* vb = static_cast<const uint8_t*>(p.v_pool);
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
-      const uint64_t off = static_cast<uint64_t>(ids.row[i]) * (D * ESZ) + c * 16;
+      const int row = static_cast<int>(ids.row[i]);
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        out.k[i][j] = *reinterpret_cast<const uint4*>(kb + off + j * (LPT * 16));
-        out.v[i][j] = *reinterpret_cast<const uint4*>(vb + off + j * (LPT * 16));
+        out.k[i][j] = __builtin_bit_cast(uint4, bsr_struct_load_b128(kr, row, c * 16 + j * (LPT * 16), 0, 0));
+        out.v[i][j] = __builtin_bit_cast(uint4, bsr_struct_load_b128(vr, row, c * 16 + j * (LPT * 16), 0, 0));
       }
     }
   }
@@ -230,6 +230,9 @@ struct DecodeBody {
     // the loop head reuses and force a full wait there).  The id buffers start
     // at the row of the chunk's first key, and loads past the end are clamped to
     // its last key, so every load is in bounds and no load sits behind a branch.
+    const __amdgpu_buffer_rsrc_t krs = row_rsrc(p.k_pool, D * ESZ);
+    const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, D * ESZ);
+    const __amdgpu_buffer_rsrc_t irs = row_rsrc(p.kv_indices, 0);
     const int ntok = it.kv_end - it.kv_begin;
     const int ntiles = (ntok + TILE - 1) / TILE;
     const int nt_w = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
@@ -237,7 +240,7 @@ struct DecodeBody {
       Pids p0, p1, p2;
       Kv k0 = {}, k1 = {}, k2 = {};  // warm-up steps read these before any load lands
       {
-        const uint32_t first = p.kv_indices[it.page_begin + it.kv_begin / p.page_size];
+        const uint32_t first = load_u32(irs, it.page_begin + it.kv_begin / p.page_size);
         const uint32_t row0 = (first * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head)) *
                                   static_cast<uint32_t>(p.page_size) +
                               static_cast<uint32_t>(it.kv_begin % p.page_size);
@@ -248,16 +251,16 @@ struct DecodeBody {
       int j = -3;
       asm volatile("" : "+s"(j));  // keep the warm-up steps inside the loop
       while (true) {
-        load_pids(p, it, t0 + (j + 3) * kWaves, grp, p0);
-        load_kv(p, it, c, p2, k2);
+        load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p0);
+        load_kv(krs, vrs, c, p2, k2);
         step(p, it, t0 + j * kWaves, grp, j >= 0, q, k0, st);
         if (++j >= nt_w) break;
-        load_pids(p, it, t0 + (j + 3) * kWaves, grp, p1);
-        load_kv(p, it, c, p0, k0);
+        load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p1);
+        load_kv(krs, vrs, c, p0, k0);
         step(p, it, t0 + j * kWaves, grp, j >= 0, q, k1, st);
         if (++j >= nt_w) break;
-        load_pids(p, it, t0 + (j + 3) * kWaves, grp, p2);
-        load_kv(p, it, c, p1, k1);
+        load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p2);
+        load_kv(krs, vrs, c, p1, k1);
         step(p, it, t0 + j * kWaves, grp, j >= 0, q, k2, st);
         if (++j >= nt_w) break;
       }
