@@ -238,7 +238,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   // partial states: at most 2 * #WG chunks of split units, each at most one tile
   // of folded rows (paper Appendix D.3), plus one state per format for tokens of
   // composed formats
-  const int64_t tile_max = bsr::kMfmaTiles[sizeof(bsr::kMfmaTiles) / sizeof(bsr::kMfmaTiles[0]) - 1];
+  const int64_t tile_max = bsr::mfma_tile(cfg->head_dim);
   pc.max_partial_rows = cfg->max_partial_rows > 0
                             ? cfg->max_partial_rows
                             : 2LL * max_wg * tile_max + 2LL * cfg->max_total_qo * g;

@@ -34,12 +34,11 @@ inline void add_decode(std::vector<KernelEntry>* out) {
                   kDecodeWgPerCu});
 }
 
-// MFMA kernels: two workgroups per CU for D <= 128, so that one workgroup's
-// softmax and gather run while the other's matrix products do (the body fits 256
-// registers per lane there); D = 256 holds a 128-float accumulator per lane and
-// runs one workgroup per CU.
+// MFMA kernels: two workgroups per CU, so that one workgroup's softmax and
+// gather run while the other's matrix products do (both MFMA bodies fit 256
+// registers per lane).
 template <int D>
-constexpr int kMfmaOcc = D <= 128 ? 2 : 1;
+constexpr int kMfmaOcc = 2;
 
 template <int D, bool CAP>
 inline void add_mfma(std::vector<KernelEntry>* out) {

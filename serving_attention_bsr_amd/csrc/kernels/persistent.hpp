@@ -24,6 +24,7 @@
 #include "decode.hpp"
 #include "merge.hpp"
 #include "prefill.hpp"
+#include "prefill16.hpp"
 
 namespace bsr {
 
@@ -35,7 +36,8 @@ template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND>
 struct PersistentKernel {
   static_assert(KIND == kKindDecode || BF16, "the MFMA body is bf16 only");
   using Decode = DecodeBody<D, BF16, ROWS, TB, CAP>;
-  using Mfma = MfmaBody<D, CAP>;
+  // 32 rows per wavefront up to D = 128; 16 rows (two workgroups per CU) at D = 256
+  using Mfma = typename std::conditional<D == 256, MfmaBody16<D, CAP>, MfmaBody<D, CAP>>::type;
   using Merge = MergeBody<D, BF16>;
   static constexpr int LDS_FLOATS =
       cmax(Merge::LDS_FLOATS, cmax(KIND == kKindMfma ? 0 : Decode::LDS_FLOATS,

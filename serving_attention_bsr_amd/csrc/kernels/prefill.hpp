@@ -41,7 +41,7 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 template <int D, bool CAP>
 struct MfmaBody {
   static constexpr int BR = 128;           // folded rows per item
-  static constexpr int BC = D == 256 ? 32 : 64;  // keys per tile (fewer registers at D = 256)
+  static constexpr int BC = 64;            // keys per tile
   static constexpr int KB = BC / 32;       // 32-key blocks per tile
   static constexpr int DK = D / 16;        // MFMA k-steps over D for S^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -58,7 +58,7 @@ struct MfmaBody {
   static constexpr int STAGE = BC * (KPAD + VPAD);   // bf16 elements of one buffer
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
-  static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+  static_assert(D == 64 || D == 128, "head_dim (D = 256 uses the 16-row body)");
 
 
   struct Loads {

@@ -1,0 +1,312 @@
+// prefill16.hpp -- MFMA attention body with 16 folded rows per wavefront, for
+// head_dim 256.
+//
+// Same method as prefill.hpp (Core mechanisms 3 and 4 of the FlashInfer explainer
+// page, paper sections 3.2 and 3.2.2; GQA folding, paper Appendix A): gathered KV
+// tiles in LDS, S^T = K Q^T and O^T += V^T P^T on the matrix cores, base-2 online
+// softmax in between.  At D = 256 a 32-row wavefront needs a 128-float
+// accumulator and 64 registers of Q per lane, which leaves one wavefront per
+// SIMD.  Here each wavefront owns 16 rows and uses v_mfma_f32_16x16x32_bf16, so
+// the accumulator is 64 floats and Q 32 registers: two workgroups fit per CU and
+// one workgroup's softmax and gather overlap the other's products.
+//
+// Lane layout of v_mfma_f32_16x16x32_bf16 (measured on gfx950 with a probe):
+// A: lane l holds A[l % 16][8 (l / 16) + j], B: lane l holds B[8 (l / 16) + j][l % 16]
+// (j = 0..7), C: lane l holds C[4 (l / 16) + i][l % 16] (i = 0..3).
+//
+// A workgroup (4 wavefronts) owns 64 folded rows; wavefront w owns rows
+// 16w..16w+15.  Per tile of 32 keys:
+//   * K and V rows are gathered (buffer loads into registers one tile ahead, page
+//     ids two tiles ahead) into one of two padded row-major LDS buffers;
+//   * S^T = K Q^T per 16-key block kb: each lane then holds keys
+//     16 kb + 4 (l / 16) + i of query row l % 16, so a row's values sit in the four
+//     lanes l % 16 + 16 q and the row max and sum take two cross-lane steps;
+//   * O^T += V^T P^T with one 32-key MFMA step per 16-row block of D: the P
+//     registers are the B operand as the S^T results left them (MFMA k index
+//     8 (l / 16) + j is key 4 (l / 16) + j for j < 4 and 16 + 4 (l / 16) + j - 4
+//     otherwise), and V^T is read in that key order with the LDS transpose read.
+#pragma once
+
+#include "common.hpp"
+
+namespace bsr {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, bool CAP>
+struct MfmaBody16 {
+  static constexpr int BR = 64;            // folded rows per item
+  static constexpr int BC = 32;            // keys per tile
+  static constexpr int KB = BC / 16;       // 16-key blocks of S^T
+  static constexpr int DK = D / 32;        // MFMA k-steps over D for S^T
+  static constexpr int DB = D / 16;        // 16-row blocks of O^T
+  static constexpr int NQ = BC / 4;        // key quads per tile
+  static constexpr int NCH = D / 8;        // 16-byte chunks per row
+  static constexpr int TASKS = NQ * NCH;   // (quad, chunk) load tasks per tile
+  static constexpr int TPT = (TASKS + kWgThreads - 1) / kWgThreads;
+  static constexpr int KPAD = D + 8;       // K: 16 rows of a pass land 4 banks apart
+  static constexpr int VPAD = D + 16;      // V: 8 consecutive rows on distinct bank eighths
+  static constexpr int STAGE = BC * (KPAD + VPAD);
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
+  static_assert(TASKS % kWgThreads == 0, "whole load tasks per thread");
+
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+  struct Loads {
+    u32x4_t k[TPT][4];
+    u32x4_t v[TPT][4];
+  };
+  struct Rows {
+    uint32_t row[TPT][4];
+  };
+
+  static __device__ __forceinline__ void task_of(int i, int& qd, int& ch) {
+    const int task = threadIdx.x + i * kWgThreads;
+    qd = task / NCH;
+    ch = task % NCH;
+  }
+
+  static __device__ __forceinline__ void load_rows(const RunParams& p, __amdgpu_buffer_rsrc_t ir,
+                                                   const WorkItem& it, int tile, Rows& out) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      int qd, ch;
+      task_of(i, qd, ch);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int tau = it.kv_begin + tile * BC + 4 * qd + j;
+        tau = min(tau, it.kv_end - 1);
+        const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+        const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+        const uint32_t page = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+        // (page * H_kv + head) * P + slot
+        out.row[i][j] = page * static_cast<uint32_t>(p.h_kv * p.page_size) +
+                        (static_cast<uint32_t>(it.kv_head * p.page_size) + slot);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                                 const Rows& rows, Loads& out) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      int qd, ch;
+      task_of(i, qd, ch);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = static_cast<int>(rows.row[i][j]);
+        out.k[i][j] = bsr_struct_load_b128(kr, row, ch * 16, 0, 0);
+        out.v[i][j] = bsr_struct_load_b128(vr, row, ch * 16, 0, 0);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void store_lds(const Loads& in, uint16_t* lk, uint16_t* lv) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      int qd, ch;
+      task_of(i, qd, ch);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * qd + j;
+        *reinterpret_cast<u32x4_t*>(lk + r * KPAD + 8 * ch) = in.k[i][j];
+        *reinterpret_cast<u32x4_t*>(lv + r * VPAD + 8 * ch) = in.v[i][j];
+      }
+    }
+  }
+
+  static __device__ __forceinline__ i16x4_t read_tr(const uint16_t* addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const_cast<uint16_t*>(addr)));
+  }
+
+  // S^T = K Q^T: block kb covers keys 16 kb .. 16 kb + 15.
+  static __device__ __forceinline__ void qk(const uint16_t* lk, const bf16x8_t (&qreg)[DK], int r16, int grp,
+                                            f32x4_t (&s)[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + (16 * kb + r16) * KPAD + 32 * ks + 8 * grp));
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], s[kb], 0, 0, 0);
+      }
+    }
+  }
+
+  // Soft-cap (base 2) and the chunk-end / causal mask of tile t.
+  static __device__ __forceinline__ void cap_and_mask(const RunParams& p, const WorkItem& it, int t, int t_local,
+                                                      int grp, f32x4_t (&s)[KB]) {
+    if constexpr (CAP) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kb][i] = p.cap_log2 * tanh_exp(s[kb][i] * p.sm_scale * p.cap_inv);
+    }
+    const int tile_base = it.kv_begin + t * BC;
+    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit) {
+      asm volatile("");  // keep this a branch: only boundary tiles pay for the mask
+      // key 16 kb + 4 grp + i of the tile is visible up to the chunk end and this
+      // row's causal limit
+      const int lim = min(it.kv_end - 1, it.causal_limit + t_local) - tile_base - 4 * grp;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * kb + i > lim) s[kb][i] = kNegInf;
+    }
+  }
+
+  // Online softmax of one tile; returns the accumulator factor.  m_run is the
+  // row's running max (the same in the row's four lanes), l_run this lane's share
+  // of the running sum.
+  static __device__ __forceinline__ float softmax(const f32x4_t (&s)[KB], float c, float& m_run, float& l_run,
+                                                  bf16x8_t& pb) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, s[kb][i]);
+    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32)) * c;
+    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = fast_exp2(__builtin_fmaf(s[kb][i], c, -m_use));
+        psum += e;
+        pb[4 * kb + i] = static_cast<__bf16>(e);
+      }
+    }
+    l_run = l_run * alpha + psum;
+    return alpha;
+  }
+
+  static __device__ __forceinline__ void rescale(float alpha, f32x4_t (&acc)[DB]) {
+    if (__ballot(alpha != 1.0f) != 0) {
+      asm volatile("");  // a real branch: most tiles leave the running maxima unchanged
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+    }
+  }
+
+  // O^T += V^T P^T.  The A operand lane (16 db + l % 16, group l / 16) needs V^T at
+  // keys 4 (l / 16) + 0..3, then 16 + 4 (l / 16) + 0..3.  With the transpose read,
+  // lane l of a 16-lane group receives element l & 3 of the 4-element rows
+  // addressed by lanes 4 e + l / 4, so lane s addresses key base + s / 4 at
+  // d = 16 db + 4 (s & 3): key_off and d_off below.
+  static __device__ __forceinline__ void pv(const uint16_t* lv, const bf16x8_t& pb, int key_off, int d_off,
+                                            f32x4_t (&acc)[DB]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = 16 * db + d_off;
+      const i16x4_t lo = read_tr(lv + key_off * VPAD + d);
+      const i16x4_t hi = read_tr(lv + (16 + key_off) * VPAD + d);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[db], 0, 0, 0);
+    }
+  }
+
+  template <typename Emit>
+  static __device__ void run(const RunParams& p, const WorkItem& it, float* lds_f, Emit&& emit) {
+    uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_f);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15;     // query row of this lane within the wavefront
+    const int grp = lane >> 4;     // lane group: k block of the operands, key quad of S^T
+    const int g = p.group;
+    const int rows_valid = it.qo_count * g;
+    const int rho = wave * 16 + r16;
+    const bool row_ok = rho < rows_valid;
+    const int t_local = rho / g;
+    const int key_off = 4 * grp + (r16 >> 2);
+    const int d_off = 4 * (r16 & 3);
+
+    // Q rows as the B operand: Q[rho][32 ks + 8 grp + 0..7]
+    bf16x8_t qreg[DK];
+    {
+      const uint16_t* qb = static_cast<const uint16_t*>(p.q);
+      const int64_t qrow = static_cast<int64_t>(it.qo_begin + t_local) * p.h_qo + it.kv_head * g + rho % g;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qb + qrow * D + 32 * ks + 8 * grp);
+        qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+
+    f32x4_t acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = kNegInf;
+    const float c = CAP ? 1.0f : p.scale_log2;
+    float l_run = 0.0f;
+
+    const __amdgpu_buffer_rsrc_t krs = row_rsrc(p.k_pool, D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, D * 2);
+    const __amdgpu_buffer_rsrc_t irs = row_rsrc(p.kv_indices, 0);
+    const int ntok = it.kv_end - it.kv_begin;
+    const int ntiles = (ntok + BC - 1) / BC;
+    Rows rows_next;
+    Loads regs;
+    // Two buffers: tile t lives in buffer t % 2; the registers carry tile t + 1
+    // while tile t is computed and go to the other buffer at the next step.
+    if (ntiles > 0) {
+      load_rows(p, irs, it, 0, rows_next);
+      load_kv(krs, vrs, rows_next, regs);
+      store_lds(regs, lds_h, lds_h + BC * KPAD);
+      if (ntiles > 1) {
+        load_rows(p, irs, it, 1, rows_next);
+        load_kv(krs, vrs, rows_next, regs);
+        load_rows(p, irs, it, ntiles > 2 ? 2 : 1, rows_next);
+      }
+    }
+    for (int t = 0; t < ntiles; ++t) {
+      __syncthreads();
+      const uint16_t* lk = lds_h + (t & 1) * STAGE;
+      if (t + 1 < ntiles) {
+        uint16_t* nk = lds_h + ((t + 1) & 1) * STAGE;
+        store_lds(regs, nk, nk + BC * KPAD);
+        if (t + 2 < ntiles) {
+          load_kv(krs, vrs, rows_next, regs);
+          load_rows(p, irs, it, t + 3 < ntiles ? t + 3 : t + 2, rows_next);
+        }
+      }
+      f32x4_t s[KB];
+      qk(lk, qreg, r16, grp, s);
+      cap_and_mask(p, it, t, t_local, grp, s);
+      bf16x8_t pb;
+      const float alpha = softmax(s, c, m_run, l_run, pb);
+      rescale(alpha, acc);
+      pv(lk + BC * KPAD, pb, key_off, d_off, acc);
+    }
+
+    // result: this lane holds O^T[16 db + 4 grp + i][rho]; the row's sum is spread
+    // over its four lanes
+    float l_tot = l_run + shfl_xor_f(l_run, 16);
+    l_tot += shfl_xor_f(l_tot, 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse2 = l_tot > 0.0f ? m_run + fast_log2(l_tot) : kNegInf;
+    if (row_ok) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + 4 * grp;
+        emit(rho, d, acc[db][0] * inv, acc[db][1] * inv, lse2);
+        emit(rho, d + 2, acc[db][2] * inv, acc[db][3] * inv, lse2);
+      }
+    }
+    __syncthreads();  // LDS free for the next item
+  }
+};
+
+}  // namespace bsr

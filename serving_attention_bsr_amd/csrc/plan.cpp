@@ -451,14 +451,9 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       q_tile = decode_rows;
     } else {
       kernel = any_decode ? kKindMixed : kKindMfma;
-      const int64_t mean = ceil_div(wide_rows_sum, wide_count);
-      int32_t tile = kMfmaTiles[sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]) - 1];
-      for (int32_t t : kMfmaTiles) {
-        if (t >= mean) {
-          tile = t;
-          break;
-        }
-      }
+      // the kernels implement one MFMA tile height per head dim (the smallest tile
+      // at least the mean folded length, from a menu of one)
+      const int32_t tile = mfma_tile(cfg.head_dim);
       if (g > tile) {
         *err = "query heads per KV head exceed the MFMA tile height";
         return BSR_ERR_UNSUPPORTED;

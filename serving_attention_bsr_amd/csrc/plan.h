@@ -57,8 +57,9 @@ constexpr int kChunkGranule = 64;
 // The planner also tries L_kv / k for k up to this and keeps the smallest
 // predicted makespan (the pages' L_kv unless another is clearly better).
 constexpr int kChunkCandidates = 4;
-// MFMA tile heights (folded rows) the kernels implement, smallest first.
-constexpr int kMfmaTiles[] = {128};
+// MFMA tile height (folded rows) of the kernels: 32 rows per wavefront up to
+// D = 128, 16 rows per wavefront at D = 256.
+inline int32_t mfma_tile(int32_t head_dim) { return head_dim == 256 ? 64 : 128; }
 
 // Returns 0 and fills out, or a bsr_status code with a message in err.
 int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t total_qo,

@@ -35,6 +35,8 @@ SWEEP = [
     ("mfma_d128_causal_p3_split", [300, 33], [700, 33], 32, 8, 128, 3, "bf16", True, 0.0, 8),
     ("mfma_d64_g1_nocausal", [129, 64], [65, 300], 4, 4, 64, 16, "bf16", False, 0.0, 0),
     ("mfma_d256_g4_cap", [50, 3], [400, 1000], 16, 4, 256, 16, "bf16", False, 20.0, 0),
+    # D = 256 runs the 16-row body: causal, several 64-row tiles, a split chunk
+    ("mfma_d256_causal_p1_split", [90, 17], [600, 17], 16, 4, 256, 1, "bf16", True, 0.0, 8),
     ("mfma_d128_g8_causal", [33, 200], [40, 200], 16, 2, 128, 2, "bf16", True, 0.0, 0),
     ("mixed_decode_prefill", [1, 50, 1, 3], [500, 120, 77, 3], 32, 8, 128, 4, "bf16", True, 0.0, 16),
     ("mfma_empty_kv_rows", [20, 5], [0, 9], 8, 2, 128, 16, "bf16", False, 0.0, 0),
