@@ -11,12 +11,14 @@
 //
 // A whole workgroup merges one task (g folded rows of one query token) at a time.
 // The contraction sits at the tail of the kernel, so it is organised for latency:
-// each source's ready stamp is polled by its own thread; the sources' LSEs are
-// read in parallel into LDS (max pass, then weight pass); the partial outputs are
-// read as 16-byte loads, four sources per step, by threads split into source
-// groups.  A task thus costs a few memory round trips however many sources it
-// has.  Within a source group the sum runs in map order and the groups are added
-// in a fixed order, so the result is deterministic.
+// each source's ready stamp is polled by its own thread, then a single pass
+// folds the sources in with a running maximum (online ⊕): each thread owns
+// float4 slots of the g rows and loads the LSE and partial outputs of a batch of
+// sources together, so a task costs about one memory round trip per batch.  When
+// the rows have fewer slots than the workgroup has threads, the threads split
+// into source groups (source s goes to group s mod groups) whose states are
+// combined in group order through LDS.  Sources are folded in map order within a
+// group, so the result is deterministic.
 #pragma once
 
 #include "common.hpp"
@@ -24,12 +26,14 @@
 namespace bsr {
 
 constexpr int kMergeMaxGroup = 16;   // query heads per KV head the merge supports
-constexpr int kMergeSrcPass = 256;   // sources staged in LDS per pass
 
 template <int D, bool BF16>
 struct MergeBody {
-  // LDS floats: staged LSE/weights, group partial sums, row max and row sums.
-  static constexpr int LDS_FLOATS = kMergeSrcPass * kMergeMaxGroup + kWgThreads * 4 + 2 * kMergeMaxGroup;
+  static constexpr int MAX_SLOTS = kMergeMaxGroup * D / 4;                       // float4 slots of a task
+  static constexpr int KSLOTS = (MAX_SLOTS + kWgThreads - 1) / kWgThreads;       // slots per thread, at most
+  static constexpr int SB = KSLOTS >= 4 ? 2 : (KSLOTS >= 2 ? 4 : 8);            // sources per batch
+  // LDS floats: per-thread group states (m, l, acc) for the cross-group combine
+  static constexpr int LDS_FLOATS = kWgThreads * 6;
 
   // Wait (bounded) for the ready stamps of a task's sources, one thread per
   // source; false if one never came.  All threads of the workgroup take part.
@@ -42,130 +46,130 @@ struct MergeBody {
   }
 
   // Merge one task (all threads).  The caller has waited and acquired.
-  static __device__ void run(const RunParams& p, const MergeTask& t, const MergeSrc* srcs,
-                             float* lds) {
+  static __device__ void run(const RunParams& p, const MergeTask& t, const MergeSrc* srcs, float* lds) {
     const int g = p.group;
     const int n = t.src_count;
     const MergeSrc* src = srcs + t.src_begin;
     const float* po = reinterpret_cast<const float*>(p.ws + p.partial_o_off);
     const float* pl = reinterpret_cast<const float*>(p.ws + p.partial_lse_off);
-    float* stage = lds;                                      // [kMergeSrcPass][g]
-    float* part = lds + kMergeSrcPass * kMergeMaxGroup;      // [kWgThreads] float4
-    float* rmax = part + kWgThreads * 4;                     // [g]
-    float* rsum = rmax + kMergeMaxGroup;                     // [g]
     const int tid = threadIdx.x;
-    // float4 slots of the g rows of one token; threads split into source groups
     const int slots = g * D / 4;
     const int groups = slots >= kWgThreads ? 1 : kWgThreads / slots;
     const int slot0 = tid % slots;
     const int grp = tid / slots;
+    const bool active = grp < groups;
 
-    // pass 1: row maxima of LSE2
-    float my_max = kNegInf;
-    for (int base = 0; base < n; base += kMergeSrcPass) {
-      const int cnt = min(kMergeSrcPass, n - base);
-      for (int i = tid; i < cnt * g; i += kWgThreads) stage[i] = pl[src[base + i / g].partial_row + i % g];
-      __syncthreads();
-      if (tid < g)
-        for (int s = 0; s < cnt; ++s) my_max = __builtin_fmaxf(my_max, stage[s * g + tid]);
-      __syncthreads();
+    // per slot k: running max (base 2), sum of weights, weighted sum of outputs
+    float m[KSLOTS], l[KSLOTS];
+    float4 acc[KSLOTS];
+    int row[KSLOTS], dcol[KSLOTS];
+    bool has[KSLOTS];
+#pragma unroll
+    for (int k = 0; k < KSLOTS; ++k) {
+      const int slot = slot0 + k * kWgThreads;
+      has[k] = active && (k == 0 || slots > kWgThreads) && slot < slots;
+      row[k] = has[k] ? (slot * 4) / D : 0;
+      dcol[k] = has[k] ? (slot * 4) % D : 0;
+      m[k] = kNegInf;
+      l[k] = 0.0f;
+      acc[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    if (tid < g) rmax[tid] = my_max;
-    __syncthreads();
-
-    // pass 2: weights 2^(lse - max), their row sums, and the weighted outputs
-    float4 acc[4];
+    if (active) {
+      // sources grp, grp + groups, ... in batches of SB loaded together; past the
+      // end a batch repeats the group's last source with weight zero
+      const int mine = n > grp ? (n - grp + groups - 1) / groups : 0;
+      for (int b = 0; b < mine; b += SB) {
+        float ls[SB][KSLOTS];
+        float4 os[SB][KSLOTS];
+        bool live[SB];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    float my_sum = 0.0f;
-    for (int base = 0; base < n; base += kMergeSrcPass) {
-      const int cnt = min(kMergeSrcPass, n - base);
-      for (int i = tid; i < cnt * g; i += kWgThreads) {
-        const float m = rmax[i % g];
-        const float l = pl[src[base + i / g].partial_row + i % g];
-        stage[i] = m == kNegInf ? 0.0f : fast_exp2(l - m);
-      }
-      __syncthreads();
-      if (tid < g)
-        for (int s = 0; s < cnt; ++s) my_sum += stage[s * g + tid];
-      if (grp < groups) {
-        // four sources per step, loads issued together; past-the-end sources are
-        // clamped to the last one with weight zero
-        for (int s = grp; s < cnt; s += 4 * groups) {
-          int sj[4];
-          float wsel[4];
+        for (int j = 0; j < SB; ++j) {
+          live[j] = b + j < mine;
+          const int s = grp + groups * min(b + j, mine - 1);
+          const int prow = src[s].partial_row;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int sv = s + j * groups;
-            sj[j] = min(sv, cnt - 1);
-            wsel[j] = sv < cnt ? 1.0f : 0.0f;
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int slot = slot0 + k * kWgThreads;
-            if (k * kWgThreads < slots && slot < slots) {
-              const int r = (slot * 4) / D;
-              const int d = (slot * 4) % D;
-              float4 v[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                v[j] = *reinterpret_cast<const float4*>(
-                    po + static_cast<int64_t>(src[base + sj[j]].partial_row + r) * D + d);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float w = wsel[j] * stage[sj[j] * g + r];
-                acc[k].x = __builtin_fmaf(w, v[j].x, acc[k].x);
-                acc[k].y = __builtin_fmaf(w, v[j].y, acc[k].y);
-                acc[k].z = __builtin_fmaf(w, v[j].z, acc[k].z);
-                acc[k].w = __builtin_fmaf(w, v[j].w, acc[k].w);
-              }
-            }
+          for (int k = 0; k < KSLOTS; ++k) {
+            if (!has[k]) continue;
+            ls[j][k] = pl[prow + row[k]];
+            os[j][k] = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(prow + row[k]) * D + dcol[k]);
           }
         }
+#pragma unroll
+        for (int k = 0; k < KSLOTS; ++k) {
+          if (!has[k]) continue;
+          float mb = m[k];
+#pragma unroll
+          for (int j = 0; j < SB; ++j)
+            if (live[j]) mb = __builtin_fmaxf(mb, ls[j][k]);
+          const float m_use = mb == kNegInf ? 0.0f : mb;
+          const float sc = fast_exp2(m[k] - m_use);
+          l[k] *= sc;
+          acc[k].x *= sc;
+          acc[k].y *= sc;
+          acc[k].z *= sc;
+          acc[k].w *= sc;
+#pragma unroll
+          for (int j = 0; j < SB; ++j) {
+            const float w = live[j] ? fast_exp2(ls[j][k] - m_use) : 0.0f;
+            l[k] += w;
+            acc[k].x = __builtin_fmaf(w, os[j][k].x, acc[k].x);
+            acc[k].y = __builtin_fmaf(w, os[j][k].y, acc[k].y);
+            acc[k].z = __builtin_fmaf(w, os[j][k].z, acc[k].z);
+            acc[k].w = __builtin_fmaf(w, os[j][k].w, acc[k].w);
+          }
+          m[k] = mb;
+        }
       }
-      __syncthreads();
     }
-    if (tid < g) rsum[tid] = my_sum;
-    // source groups are added in a fixed order (groups > 1 only when one slot
-    // per thread covers the rows)
+    // source groups are combined in group order (groups > 1 only with one slot
+    // per thread)
     if (groups > 1) {
-      reinterpret_cast<float4*>(part)[tid] = acc[0];
+      if (active) {
+        float* st = lds + tid * 6;
+        st[0] = m[0];
+        st[1] = l[0];
+        st[2] = acc[0].x;
+        st[3] = acc[0].y;
+        st[4] = acc[0].z;
+        st[5] = acc[0].w;
+      }
       __syncthreads();
       if (grp == 0) {
         for (int q = 1; q < groups; ++q) {
-          const float4 v = reinterpret_cast<const float4*>(part)[q * slots + slot0];
-          acc[0].x += v.x;
-          acc[0].y += v.y;
-          acc[0].z += v.z;
-          acc[0].w += v.w;
+          const float* st = lds + (q * slots + slot0) * 6;
+          const float mq = st[0];
+          const float mn = __builtin_fmaxf(m[0], mq);
+          const float m_use = mn == kNegInf ? 0.0f : mn;
+          const float a = fast_exp2(m[0] - m_use), bq = fast_exp2(mq - m_use);
+          l[0] = l[0] * a + st[1] * bq;
+          acc[0].x = acc[0].x * a + st[2] * bq;
+          acc[0].y = acc[0].y * a + st[3] * bq;
+          acc[0].z = acc[0].z * a + st[4] * bq;
+          acc[0].w = acc[0].w * a + st[5] * bq;
+          m[0] = mn;
         }
       }
     }
-    __syncthreads();
     if (grp == 0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int slot = slot0 + k * kWgThreads;
-        if (k * kWgThreads < slots && slot < slots) {
-          const int r = (slot * 4) / D;
-          const int d = (slot * 4) % D;
-          const float z = rsum[r];
-          const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-          const int64_t orow = static_cast<int64_t>(t.qo_row) * p.h_qo + t.kv_head * g + r;
-          const float o0 = acc[k].x * inv, o1 = acc[k].y * inv, o2 = acc[k].z * inv, o3 = acc[k].w * inv;
-          if constexpr (BF16) {
-            uint2 pk;
-            pk.x = pack_bf16x2(o0, o1);
-            pk.y = pack_bf16x2(o2, o3);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow * D + d) = pk;
-          } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.o) + orow * D + d) = make_float4(o0, o1, o2, o3);
-          }
-          if (d == 0 && p.lse != nullptr) p.lse[orow] = z > 0.0f ? (rmax[r] + fast_log2(z)) * kLn2 : kNegInf;
+      for (int k = 0; k < KSLOTS; ++k) {
+        if (!has[k]) continue;
+        const float z = l[k];
+        const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+        const int64_t orow = static_cast<int64_t>(t.qo_row) * p.h_qo + t.kv_head * g + row[k];
+        const float o0 = acc[k].x * inv, o1 = acc[k].y * inv, o2 = acc[k].z * inv, o3 = acc[k].w * inv;
+        if constexpr (BF16) {
+          uint2 pk;
+          pk.x = pack_bf16x2(o0, o1);
+          pk.y = pack_bf16x2(o2, o3);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow * D + dcol[k]) = pk;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.o) + orow * D + dcol[k]) = make_float4(o0, o1, o2, o3);
         }
+        if (dcol[k] == 0 && p.lse != nullptr) p.lse[orow] = z > 0.0f ? (m[k] + fast_log2(z)) * kLn2 : kNegInf;
       }
     }
-    __syncthreads();
+    __syncthreads();  // LDS and the next task
   }
 };
 
