@@ -104,6 +104,23 @@ __device__ __forceinline__ int32_t* plan_i32(uint8_t* ws, int32_t off) {
 
 constexpr int kMaxSpins = 1 << 21;
 
+// s_waitcnt operand (gfx9 encoding) that waits for every outstanding vector
+// memory access: vmcnt 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Device-scope loads of partial states (read past the per-XCD L2 caches).
+__device__ __forceinline__ float load_dev_f32(const float* p) {
+  return __uint_as_float(
+      __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float4 load_dev_f32x4(const float* p) {
+  const uint64_t a = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b =
+      __hip_atomic_load(reinterpret_cast<const uint64_t*>(p) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float(static_cast<uint32_t>(a)), __uint_as_float(static_cast<uint32_t>(a >> 32)),
+                     __uint_as_float(static_cast<uint32_t>(b)), __uint_as_float(static_cast<uint32_t>(b >> 32)));
+}
+
 // Wait (bounded) until *flag == epoch.  Returns false if the bound expired.
 __device__ __forceinline__ bool wait_flag(const int32_t* flag, int32_t epoch) {
   int spins = 0;

@@ -45,7 +45,8 @@ struct MergeBody {
     return ok;
   }
 
-  // Merge one task (all threads).  The caller has waited and acquired.
+  // Merge one task (all threads).  The caller has waited for the sources' stamps;
+  // states are read with device-scope loads.
   static __device__ void run(const RunParams& p, const MergeTask& t, const MergeSrc* srcs, float* lds) {
     const int g = p.group;
     const int n = t.src_count;
@@ -90,8 +91,8 @@ struct MergeBody {
 #pragma unroll
           for (int k = 0; k < KSLOTS; ++k) {
             if (!has[k]) continue;
-            ls[j][k] = pl[prow + row[k]];
-            os[j][k] = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(prow + row[k]) * D + dcol[k]);
+            ls[j][k] = load_dev_f32(pl + prow + row[k]);
+            os[j][k] = load_dev_f32x4(po + static_cast<int64_t>(prow + row[k]) * D + dcol[k]);
           }
         }
 #pragma unroll

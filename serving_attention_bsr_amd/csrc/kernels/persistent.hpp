@@ -7,11 +7,16 @@
 // unsplit ones write O/LSE directly; the contraction of partial states runs in
 // the same kernel, in the order the plan fixed, without atomic accumulation.
 //
-// Ordering between a partial's writer and its merger uses release/acquire ready
-// stamps, not read-modify-write: after its attention items a workgroup releases
-// once and stores the run's epoch into the flag of each partial state it wrote;
-// a merging workgroup waits until the flags of its sources equal the epoch, then
-// acquires once.  Each workgroup keeps its own run counter in the plan blob; the plan
+// Ordering between a partial's writer and its merger uses ready stamps, not
+// read-modify-write.  Partial states, stamps and the merger's reads of both are
+// device-scope accesses (written through to, and read from, the device's
+// coherence point, past the per-XCD L2 caches): after its attention items a
+// workgroup waits until its partial-state stores have completed, meets, and
+// stores the run's epoch into the flag of each partial state it wrote; a merging
+// workgroup waits until the flags of its sources equal the epoch, then reads the
+// states.  A device-scope release/acquire fence would instead write back and
+// invalidate whole L2 caches, which costs about 10 us per workgroup at the end of
+// a busy kernel.  Each workgroup keeps its own run counter in the plan blob; the plan
 // upload zeroes all counters and every run advances each by one, so all
 // workgroups of a run agree on its epoch and stamps of older runs never match.
 // Every workgroup finishes its attention items before it merges, and the grid
@@ -105,8 +110,12 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
       float* pl = reinterpret_cast<float*>(ws + p.partial_lse_off);
       auto emit = [&](int r, int d, float o0, float o1, float lse2) {
         const int64_t row = static_cast<int64_t>(it.partial_row) + r;
-        *reinterpret_cast<float2*>(po + row * D + d) = make_float2(o0, o1);
-        if (d == 0) pl[row] = lse2;
+        const uint64_t pair = (static_cast<uint64_t>(__float_as_uint(o1)) << 32) | __float_as_uint(o0);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(po + row * D + d), pair, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0)
+          __hip_atomic_store(reinterpret_cast<uint32_t*>(pl + row), __float_as_uint(lse2), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       };
       K::attend(p, it, lds, emit);
       any_partial = true;
@@ -126,15 +135,13 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   }
 
   BSR_STAMP(1);
-  // One release for all partial states this workgroup wrote (a release writes
-  // back the XCD's L2, so it is done once per workgroup, not per item): every
-  // wavefront releases its own stores, the workgroup meets, wavefront 0 releases
-  // again (covering what the barrier ordered before it) and stores the stamps.
+  // Stamps for the partial states this workgroup wrote: every wavefront waits
+  // until its device-scope stores have completed (vector memory counter at 0),
+  // the workgroup meets, and wavefront 0 stores the stamps.
   if (any_partial) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (threadIdx.x < 64) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       for (int32_t i = ib + static_cast<int32_t>(threadIdx.x); i < ie; i += 64) {
         const WorkItem& it = items[i];
         if (it.flags & kItemPartial)
@@ -150,12 +157,12 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   const MergeSrc* srcs = reinterpret_cast<const MergeSrc*>(ws + hdr->off_srcs);
   const int32_t mb = merge_ptr[wg], me = merge_ptr[wg + 1];
   // the workgroup waits for every source of its tasks (one thread per source),
-  // acquires once, then merges its tasks one after another
+  // then merges its tasks one after another (the merge reads the states with
+  // device-scope loads, so no cache of this XCD can hold them stale)
   bool ok = true;
   if (mb < me) {
     for (int32_t t = mb; t < me && ok; ++t) ok = K::Merge::wait(tasks[t], srcs, flags, epoch);
     BSR_STAMP(3);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __syncthreads();
     for (int32_t t = mb; t < me; ++t) K::Merge::run(p, tasks[t], srcs, lds);
   }
