@@ -81,16 +81,26 @@ struct MfmaBody {
     for (int i = 0; i < TPT; ++i) {
       int qd, ch;
       task_of(i, qd, ch);
+      const int tau0 = it.kv_begin + tile * BC + 4 * qd;
+      if (p.page_size == 1) {
+        // one key per page: no division
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int tau = it.kv_begin + tile * BC + 4 * qd + j;
-        tau = min(tau, it.kv_end - 1);
-        const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
-        const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-        const uint32_t page = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
-        // (page * H_kv + head) * P + slot
-        out.row[i][j] = page * static_cast<uint32_t>(p.h_kv * p.page_size) +
-                        (static_cast<uint32_t>(it.kv_head * p.page_size) + slot);
+        for (int j = 0; j < 4; ++j) {
+          const int tau = min(tau0 + j, it.kv_end - 1);
+          const uint32_t page = load_u32(ir, it.page_begin + tau);
+          out.row[i][j] = page * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tau = min(tau0 + j, it.kv_end - 1);
+          const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+          const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+          const uint32_t page = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+          // (page * H_kv + head) * P + slot
+          out.row[i][j] = page * static_cast<uint32_t>(p.h_kv * p.page_size) +
+                          (static_cast<uint32_t>(it.kv_head * p.page_size) + slot);
+        }
       }
     }
   }
