@@ -104,6 +104,25 @@ __device__ __forceinline__ int32_t* plan_i32(uint8_t* ws, int32_t off) {
 
 constexpr int kMaxSpins = 1 << 21;
 
+// Load of memory that no thread writes during the kernel (the plan's queues),
+// through the constant address space: uniform reads become scalar loads, which
+// can be issued ahead of use without holding vector registers.  (The host pass
+// of the single-source compile sees a plain read; it never runs this code.)
+template <typename T>
+__device__ __forceinline__ T load_invariant(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "whole dwords");
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(4))) const uint32_t c_u32;
+  c_u32* q = (c_u32*)(p);
+  uint32_t w[sizeof(T) / 4];
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(sizeof(T) / 4); ++i) w[i] = q[i];
+  return __builtin_bit_cast(T, w);
+#else
+  return *p;
+#endif
+}
+
 // s_waitcnt operand (gfx9 encoding) that waits for every outstanding vector
 // memory access: vmcnt 0, expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;

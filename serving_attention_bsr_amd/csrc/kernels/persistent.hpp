@@ -83,9 +83,12 @@ template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, int OCC>
 __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunParams p) {
   using K = PersistentKernel<D, BF16, ROWS, TB, CAP, KIND>;
   __shared__ float lds[K::LDS_FLOATS];
-  __shared__ int32_t s_epoch;
   uint8_t* ws = p.ws;
-  const PlanHeader* hdr = plan_header(ws);
+  // the whole header in one read (its fields are uniform; the empty asm keeps the
+  // offsets from being loaded separately after the check below)
+  const PlanHeader h = *plan_header(ws);
+  asm volatile("" ::"s"(h.off_epochs), "s"(h.off_item_ptr), "s"(h.off_items), "s"(h.off_flags));
+  const PlanHeader* hdr = &h;
   const int wg = blockIdx.x;
   if (wg >= hdr->num_wg) return;  // grid larger than this plan's (never by construction)
 
@@ -93,18 +96,23 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   int32_t* flags = plan_i32(ws, hdr->off_flags);
   int32_t* status = plan_i32(ws, hdr->off_status);
   BSR_STAMP(0);
-  if (threadIdx.x == 0) s_epoch = epochs[wg] + 1;
-  __syncthreads();
-  const int32_t epoch = s_epoch;
+  // the run counter is first needed after the attention items: its (uniform) load
+  // is issued here and waited for there, off the items' latency chain
+  const int32_t epoch = epochs[wg] + 1;
   const int g = p.group;
 
   // ---- attention items -------------------------------------------------------
+  // The queue is read-only during the run: scalar loads, and the next item is
+  // read while this one runs.
   const int32_t* item_ptr = plan_i32(ws, hdr->off_item_ptr);
   const WorkItem* items = reinterpret_cast<const WorkItem*>(ws + hdr->off_items);
-  const int32_t ib = item_ptr[wg], ie = item_ptr[wg + 1];
+  const int32_t ib = load_invariant(item_ptr + wg), ie = load_invariant(item_ptr + wg + 1);
   bool any_partial = false;
+  WorkItem nxt;
+  if (ib < ie) nxt = load_invariant(items + ib);
   for (int32_t i = ib; i < ie; ++i) {
-    const WorkItem it = items[i];
+    const WorkItem it = nxt;
+    if (i + 1 < ie) nxt = load_invariant(items + i + 1);
     if (it.flags & kItemPartial) {
       float* po = reinterpret_cast<float*>(ws + p.partial_o_off);
       float* pl = reinterpret_cast<float*>(ws + p.partial_lse_off);
