@@ -65,8 +65,13 @@ struct MfmaBody {
     u32x4_t k[TPT][4];
     u32x4_t v[TPT][4];
   };
+  // Page ids of this thread's rows, loaded a tile ahead of the rows themselves.  The
+  // id is kept as loaded and the row index formed only when the rows are read:
+  // arithmetic on the id right after its load would wait for every load issued
+  // before it (the vector memory counter completes in order), K/V rows included.
   struct Rows {
-    uint32_t row[TPT][4];
+    uint32_t page[TPT][4];
+    uint32_t off[TPT][4];   // head * P + slot: row = page * (H_kv * P) + off
   };
 
   static __device__ __forceinline__ void task_of(int i, int& qd, int& ch) {
@@ -87,8 +92,8 @@ struct MfmaBody {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int tau = min(tau0 + j, it.kv_end - 1);
-          const uint32_t page = load_u32(ir, it.page_begin + tau);
-          out.row[i][j] = page * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head);
+          out.page[i][j] = load_u32(ir, it.page_begin + tau);
+          out.off[i][j] = static_cast<uint32_t>(it.kv_head);
         }
       } else {
 #pragma unroll
@@ -96,17 +101,16 @@ struct MfmaBody {
           const int tau = min(tau0 + j, it.kv_end - 1);
           const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
           const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-          const uint32_t page = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
-          // (page * H_kv + head) * P + slot
-          out.row[i][j] = page * static_cast<uint32_t>(p.h_kv * p.page_size) +
-                          (static_cast<uint32_t>(it.kv_head * p.page_size) + slot);
+          out.page[i][j] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+          out.off[i][j] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
         }
       }
     }
   }
 
+  // rows_per_page = H_kv * P: pool rows between consecutive pages
   static __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                                 const Rows& rows, Loads& out) {
+                                                 uint32_t rows_per_page, const Rows& rows, Loads& out) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       int qd, ch;
@@ -114,7 +118,7 @@ struct MfmaBody {
       if (TASKS % kWgThreads != 0 && qd >= NQ) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = static_cast<int>(rows.row[i][j]);
+        const int row = static_cast<int>(rows.page[i][j] * rows_per_page + rows.off[i][j]);
         out.k[i][j] = bsr_struct_load_b128(kr, row, ch * 16, 0, 0);
         out.v[i][j] = bsr_struct_load_b128(vr, row, ch * 16, 0, 0);
       }
@@ -294,17 +298,18 @@ struct MfmaBody {
     const __amdgpu_buffer_rsrc_t krs = row_rsrc(p.k_pool, D * 2);
     const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, D * 2);
     const __amdgpu_buffer_rsrc_t irs = row_rsrc(p.kv_indices, 0);
+    const uint32_t rpp = static_cast<uint32_t>(p.h_kv * p.page_size);
     Rows rows_next;
     Loads regs;
     // Two buffers: tile t lives in buffer t % 2; the registers carry tile t + 1
     // while tile t is computed and go to the other buffer at the next step.
     if (ntiles > 0) {
       load_rows(p, irs, it, 0, rows_next);
-      load_kv(krs, vrs, rows_next, regs);
+      load_kv(krs, vrs, rpp, rows_next, regs);
       store_lds(regs, lds_h, lds_h + BC * KPAD);
       if (ntiles > 1) {
         load_rows(p, irs, it, 1, rows_next);
-        load_kv(krs, vrs, rows_next, regs);
+        load_kv(krs, vrs, rpp, rows_next, regs);
         load_rows(p, irs, it, ntiles > 2 ? 2 : 1, rows_next);
       }
     }
@@ -317,7 +322,7 @@ struct MfmaBody {
         uint16_t* nk = lds_h + ((t + 1) & 1) * STAGE;
         store_lds(regs, nk, nk + BC * KPAD);
         if (t + 2 < ntiles) {
-          load_kv(krs, vrs, rows_next, regs);
+          load_kv(krs, vrs, rpp, rows_next, regs);
           load_rows(p, irs, it, t + 3 < ntiles ? t + 3 : t + 2, rows_next);
         }
       }
