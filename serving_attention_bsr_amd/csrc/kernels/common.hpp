@@ -51,6 +51,15 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ u32x4_t bsr_struct_load_b128(__amdgpu_buffer_rsrc_t rsrc, int vindex, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
 
+// The same 16-byte row gather written straight into LDS, without passing through
+// registers: lane i of the wavefront lands at lds + 16 i (lds is wave-uniform).
+// Completion is counted by the vector memory counter like any load; the writes are
+// visible to the rest of the workgroup after that counter drains and a barrier.
+__device__ __forceinline__ void lds_gather_b128(__amdgpu_buffer_rsrc_t rsrc, void* lds, int vindex, int voffset) {
+  __builtin_amdgcn_struct_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, vindex,
+                                              voffset, 0, 0, 0);
+}
+
 // Element i of a 32-bit array through a raw buffer resource (32-bit offset).
 __device__ __forceinline__ uint32_t load_u32(__amdgpu_buffer_rsrc_t rsrc, int i) {
   return __builtin_amdgcn_raw_buffer_load_b32(rsrc, i * 4, 0, 0);

@@ -10,11 +10,12 @@
 //
 // gfx950 mapping.  A workgroup (4 wavefronts) owns 128 folded rows; wavefront w
 // owns rows 32w..32w+31.  Per tile of 64 keys:
-//   * the workgroup gathers the keys' K and V rows page by page (16-byte loads
-//     into registers one tile ahead, page ids two tiles ahead) and stages both
-//     row-major in one of two LDS buffers, so that one barrier per tile suffices;
-//     the row strides are padded so that the reads below hit distinct banks
-//     while every read address stays a per-lane base plus an immediate;
+//   * the workgroup gathers the keys' K and V rows page by page with 16-byte
+//     buffer loads that write LDS directly (one tile ahead; page ids two tiles
+//     ahead), row-major into one of two LDS buffers, so that one barrier per tile
+//     suffices and no register or LDS-store instruction carries the tile; the
+//     16-byte chunks of each row are permuted so that the reads below hit
+//     distinct banks;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //     wavefront's Q rows, held in registers for the whole item): each lane then
 //     holds one query column and 16 keys of each 32-key block, so the softmax max
@@ -45,99 +46,72 @@ struct MfmaBody {
   static constexpr int KB = BC / 32;       // 32-key blocks per tile
   static constexpr int DK = D / 16;        // MFMA k-steps over D for S^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
-  static constexpr int NQ = BC / 4;        // key quads per tile
   static constexpr int NCH = D / 8;        // 16-byte chunks per row
-  static constexpr int TASKS = NQ * NCH;   // (quad, chunk) load tasks per tile
-  static constexpr int TPT = (TASKS + kWgThreads - 1) / kWgThreads;  // tasks per thread
-  // Row strides (bf16).  K is read one row per lane, 16 lanes per pass: a stride of
-  // D + 8 moves each row by 4 banks, so 16 rows fill the 64 banks.  V is read with
-  // the transpose read, 4 consecutive keys x 64 bytes per half-wave: a stride of
-  // 16 or 48 dwords modulo 64 puts the 4 rows on 4 distinct quarters of the banks.
-  static constexpr int KPAD = D + 8;
-  static constexpr int VPAD = D + 32;
-  static constexpr int STAGE = BC * (KPAD + VPAD);   // bf16 elements of one buffer
+  static constexpr int RPI = 64 / NCH;     // rows per 1 KB gather instruction
+  static constexpr int NI = BC / RPI / kWaves;  // gather instructions per wavefront, tile and matrix
+  // Tiles are unpadded (row r at r * D elements, K then V) with the 16-byte chunks
+  // of each row permuted: chunk c of row r sits in slot c ^ swz(r), which keeps every
+  // gather instruction a contiguous 1 KB of LDS.  K is read one row per lane, 16
+  // lanes per pass, all at one chunk: swz_k puts 16 consecutive rows on the 16
+  // slots of 256 bytes (all 64 banks).  V is read with the transpose read, 4
+  // consecutive keys x 64 bytes per half-wave: swz_v puts the 4 rows' 64-byte groups
+  // on 4 distinct quarters of the banks.
+  static constexpr int STAGE = 2 * BC * D;  // bf16 elements of one buffer
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
   static_assert(D == 64 || D == 128, "head_dim (D = 256 uses the 16-row body)");
+  static_assert(NI * RPI * kWaves == BC, "whole gather instructions per wavefront");
 
+  static __device__ __forceinline__ int swz_k(int r) { return (r / (16 / NCH)) % NCH; }
+  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / (16 / NCH)) % (NCH / 4)); }
 
-  struct Loads {
-    u32x4_t k[TPT][4];
-    u32x4_t v[TPT][4];
-  };
-  // Page ids of this thread's rows, loaded a tile ahead of the rows themselves.  The
-  // id is kept as loaded and the row index formed only when the rows are read:
+  // Page ids of this lane's rows, loaded a tile ahead of the rows themselves.  The
+  // id is kept as loaded and the row index formed only when the rows are gathered:
   // arithmetic on the id right after its load would wait for every load issued
-  // before it (the vector memory counter completes in order), K/V rows included.
+  // before it (the vector memory counter completes in order).
   struct Rows {
-    uint32_t page[TPT][4];
-    uint32_t off[TPT][4];   // head * P + slot: row = page * (H_kv * P) + off
+    uint32_t page[NI];
+    uint32_t off[NI];   // head * P + slot: row = page * (H_kv * P) + off
   };
 
-  static __device__ __forceinline__ void task_of(int i, int& qd, int& ch) {
-    const int task = threadIdx.x + i * kWgThreads;
-    qd = task / NCH;
-    ch = task % NCH;
+  // Row n of this lane in the tile: RPI rows per instruction, NI instructions per
+  // wavefront, lane / NCH within the instruction.
+  static __device__ __forceinline__ int lane_row(int wave, int lane, int n) {
+    return RPI * (NI * wave + n) + lane / NCH;
   }
 
   static __device__ __forceinline__ void load_rows(const RunParams& p, __amdgpu_buffer_rsrc_t ir,
-                                                   const WorkItem& it, int tile, Rows& out) {
+                                                   const WorkItem& it, int tile, int wave, int lane, Rows& out) {
+    const int tau0 = it.kv_begin + tile * BC;
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      int qd, ch;
-      task_of(i, qd, ch);
-      const int tau0 = it.kv_begin + tile * BC + 4 * qd;
+    for (int n = 0; n < NI; ++n) {
+      const int tau = min(tau0 + lane_row(wave, lane, n), it.kv_end - 1);
       if (p.page_size == 1) {
         // one key per page: no division
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tau = min(tau0 + j, it.kv_end - 1);
-          out.page[i][j] = load_u32(ir, it.page_begin + tau);
-          out.off[i][j] = static_cast<uint32_t>(it.kv_head);
-        }
+        out.page[n] = load_u32(ir, it.page_begin + tau);
+        out.off[n] = static_cast<uint32_t>(it.kv_head);
       } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tau = min(tau0 + j, it.kv_end - 1);
-          const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
-          const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-          out.page[i][j] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
-          out.off[i][j] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
-        }
+        const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+        const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+        out.page[n] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+        out.off[n] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
       }
     }
   }
 
-  // rows_per_page = H_kv * P: pool rows between consecutive pages
-  static __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                                 uint32_t rows_per_page, const Rows& rows, Loads& out) {
+  // Gather one tile's K and V rows into a buffer (K at buf, V at buf + BC * D).
+  // rows_per_page = H_kv * P: pool rows between consecutive pages.
+  static __device__ __forceinline__ void gather(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                                uint32_t rows_per_page, const Rows& rows, uint16_t* buf, int wave,
+                                                int lane) {
+    const int slot = lane % NCH;
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      int qd, ch;
-      task_of(i, qd, ch);
-      if (TASKS % kWgThreads != 0 && qd >= NQ) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = static_cast<int>(rows.page[i][j] * rows_per_page + rows.off[i][j]);
-        out.k[i][j] = bsr_struct_load_b128(kr, row, ch * 16, 0, 0);
-        out.v[i][j] = bsr_struct_load_b128(vr, row, ch * 16, 0, 0);
-      }
-    }
-  }
-
-  // K and V row-major with padded strides.
-  static __device__ __forceinline__ void store_lds(const Loads& in, uint16_t* lk, uint16_t* lv) {
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      int qd, ch;
-      task_of(i, qd, ch);
-      if (TASKS % kWgThreads != 0 && qd >= NQ) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * qd + j;
-        *reinterpret_cast<u32x4_t*>(lk + r * KPAD + 8 * ch) = in.k[i][j];
-        *reinterpret_cast<u32x4_t*>(lv + r * VPAD + 8 * ch) = in.v[i][j];
-      }
+    for (int n = 0; n < NI; ++n) {
+      const int r = lane_row(wave, lane, n);
+      const int row = static_cast<int>(rows.page[n] * rows_per_page + rows.off[n]);
+      uint16_t* dst = buf + (NI * wave + n) * 512;
+      lds_gather_b128(kr, dst, row, 16 * (slot ^ swz_k(r)));
+      lds_gather_b128(vr, dst + BC * D, row, 16 * (slot ^ swz_v(r)));
     }
   }
 
@@ -157,9 +131,9 @@ struct MfmaBody {
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        const int r = 32 * kb + col;
+        const int r = 32 * kb + col;   // swz_k(r) == swz_k(col): 32 rows apart
         const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * KPAD + 16 * ks + 8 * half));
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * D + 8 * ((2 * ks + half) ^ swz_k(col))));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
       }
     }
@@ -244,9 +218,11 @@ struct MfmaBody {
         const int r1 = r0 + 8;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = 32 * db + d_off;
-          const i16x4_t lo = read_tr(lv + r0 * VPAD + d);
-          const i16x4_t hi = read_tr(lv + r1 * VPAD + d);
+          // chunk (32 db + d_off) / 8 of rows r0 and r1 (swz_v(r0) == swz_v(r1) == swz_v(key_off):
+          // they differ from key_off by multiples of 8)
+          const int at = 8 * ((4 * db + d_off / 8) ^ swz_v(key_off)) + d_off % 8;
+          const i16x4_t lo = read_tr(lv + r0 * D + at);
+          const i16x4_t hi = read_tr(lv + r1 * D + at);
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][st], acc[db], 0, 0, 0);
         }
@@ -299,32 +275,25 @@ struct MfmaBody {
     const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, D * 2);
     const __amdgpu_buffer_rsrc_t irs = row_rsrc(p.kv_indices, 0);
     const uint32_t rpp = static_cast<uint32_t>(p.h_kv * p.page_size);
-    Rows rows_next;
-    Loads regs;
-    // Two buffers: tile t lives in buffer t % 2; the registers carry tile t + 1
-    // while tile t is computed and go to the other buffer at the next step.
+    Rows rows;
+    // Two buffers: tile t lives in buffer t % 2.  The gather of tile t + 1 into the
+    // other buffer and the page ids of tile t + 2 are issued before tile t is
+    // computed and waited for at the next step.
     if (ntiles > 0) {
-      load_rows(p, irs, it, 0, rows_next);
-      load_kv(krs, vrs, rpp, rows_next, regs);
-      store_lds(regs, lds_h, lds_h + BC * KPAD);
-      if (ntiles > 1) {
-        load_rows(p, irs, it, 1, rows_next);
-        load_kv(krs, vrs, rpp, rows_next, regs);
-        load_rows(p, irs, it, ntiles > 2 ? 2 : 1, rows_next);
-      }
+      load_rows(p, irs, it, 0, wave, lane, rows);
+      gather(krs, vrs, rpp, rows, lds_h, wave, lane);
+      if (ntiles > 1) load_rows(p, irs, it, 1, wave, lane, rows);
     }
     for (int t = 0; t < ntiles; ++t) {
-      // tile t is in its buffer; every wavefront is done with tile t - 1, whose
-      // buffer now takes tile t + 1
+      // this wavefront's gather of tile t (and the ids of tile t + 1) has landed;
+      // after the barrier every wavefront's has, and every wavefront is done with
+      // tile t - 1, whose buffer now takes tile t + 1
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
       const uint16_t* lk = lds_h + (t & 1) * STAGE;
       if (t + 1 < ntiles) {
-        uint16_t* nk = lds_h + ((t + 1) & 1) * STAGE;
-        store_lds(regs, nk, nk + BC * KPAD);
-        if (t + 2 < ntiles) {
-          load_kv(krs, vrs, rpp, rows_next, regs);
-          load_rows(p, irs, it, t + 3 < ntiles ? t + 3 : t + 2, rows_next);
-        }
+        gather(krs, vrs, rpp, rows, lds_h + ((t + 1) & 1) * STAGE, wave, lane);
+        if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);
       }
       f32x16_t s[KB];
       qk(lk, qreg, col, half, s);
@@ -332,7 +301,7 @@ struct MfmaBody {
       bf16x8_t pb[KB][2];
       const float alpha = softmax(s, c, m_run, l_run, pb);
       rescale(alpha, acc);
-      pv(lk + BC * KPAD, pb, key_off, d_off, acc);
+      pv(lk + BC * D, pb, key_off, d_off, acc);
     }
 
     // result: this lane's column holds O^T[d][rho] for d = 32 db + 8 (r/4) + 4 half + r%4
