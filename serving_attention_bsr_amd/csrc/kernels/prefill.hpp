@@ -99,14 +99,16 @@ struct MfmaBody {
     }
   }
 
-  // Gather one tile's K and V rows into a buffer (K at buf, V at buf + BC * D).
-  // rows_per_page = H_kv * P: pool rows between consecutive pages.
+  // Gather this lane's rows N0 <= n < N1 of a tile's K and V into a buffer (K at
+  // buf, V at buf + BC * D).  rows_per_page = H_kv * P: pool rows between
+  // consecutive pages.
+  template <int N0 = 0, int N1 = NI>
   static __device__ __forceinline__ void gather(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                                 uint32_t rows_per_page, const Rows& rows, uint16_t* buf, int wave,
                                                 int lane) {
     const int slot = lane % NCH;
 #pragma unroll
-    for (int n = 0; n < NI; ++n) {
+    for (int n = N0; n < N1; ++n) {
       const int r = lane_row(wave, lane, n);
       const int row = static_cast<int>(rows.page[n] * rows_per_page + rows.off[n]);
       uint16_t* dst = buf + (NI * wave + n) * 512;
@@ -291,12 +293,16 @@ struct MfmaBody {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
       const uint16_t* lk = lds_h + (t & 1) * STAGE;
-      if (t + 1 < ntiles) {
-        gather(krs, vrs, rpp, rows, lds_h + ((t + 1) & 1) * STAGE, wave, lane);
-        if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);
-      }
+      uint16_t* nb = lds_h + ((t + 1) & 1) * STAGE;
+      // the gather of tile t + 1 is issued in two halves around the S^T products,
+      // so that the workgroups of a CU do not all queue their loads at once
+      if (t + 1 < ntiles) gather<0, NI / 2>(krs, vrs, rpp, rows, nb, wave, lane);
       f32x16_t s[KB];
       qk(lk, qreg, col, half, s);
+      if (t + 1 < ntiles) {
+        gather<NI / 2, NI>(krs, vrs, rpp, rows, nb, wave, lane);
+        if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);
+      }
       cap_and_mask(p, it, t, t_local, half, s);
       bf16x8_t pb[KB][2];
       const float alpha = softmax(s, c, m_run, l_run, pb);

@@ -16,8 +16,9 @@
 //
 // A workgroup (4 wavefronts) owns 64 folded rows; wavefront w owns rows
 // 16w..16w+15.  Per tile of 32 keys:
-//   * K and V rows are gathered (buffer loads into registers one tile ahead, page
-//     ids two tiles ahead) into one of two padded row-major LDS buffers;
+//   * K and V rows are gathered by buffer loads that write LDS directly (one tile
+//     ahead, page ids two tiles ahead) into one of two row-major LDS buffers whose
+//     16-byte chunks are permuted per row against bank conflicts;
 //   * S^T = K Q^T per 16-key block kb: each lane then holds keys
 //     16 kb + 4 (l / 16) + i of query row l % 16, so a row's values sit in the four
 //     lanes l % 16 + 16 q and the row max and sum take two cross-lane steps;
@@ -40,81 +41,65 @@ struct MfmaBody16 {
   static constexpr int KB = BC / 16;       // 16-key blocks of S^T
   static constexpr int DK = D / 32;        // MFMA k-steps over D for S^T
   static constexpr int DB = D / 16;        // 16-row blocks of O^T
-  static constexpr int NQ = BC / 4;        // key quads per tile
   static constexpr int NCH = D / 8;        // 16-byte chunks per row
-  static constexpr int TASKS = NQ * NCH;   // (quad, chunk) load tasks per tile
-  static constexpr int TPT = (TASKS + kWgThreads - 1) / kWgThreads;
-  static constexpr int KPAD = D + 8;       // K: 16 rows of a pass land 4 banks apart
-  static constexpr int VPAD = D + 16;      // V: 8 consecutive rows on distinct bank eighths
-  static constexpr int STAGE = BC * (KPAD + VPAD);
+  static constexpr int RPI = 64 / NCH;     // rows per 1 KB gather instruction
+  static constexpr int NI = BC / RPI / kWaves;  // gather instructions per wavefront, tile and matrix
+  // Unpadded tiles (row r at r * D elements, K then V) with the 16-byte chunks of
+  // each row permuted: chunk c of row r sits in slot c ^ swz(r).  K is read one row
+  // per lane, 16 lanes per pass at one chunk: swz_k puts 16 consecutive rows on
+  // the 16 slots of 256 bytes.  V is read with the transpose read, 8 consecutive
+  // keys x 32 bytes per half-wave: swz_v puts the 8 rows' 32-byte pairs of chunks
+  // on 8 distinct eighths of the banks.
+  static constexpr int STAGE = 2 * BC * D;  // bf16 elements of one buffer
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
-  static_assert(TASKS % kWgThreads == 0, "whole load tasks per thread");
+  static_assert(D == 256, "the 16-row body serves head_dim 256");
+  static_assert(NI * RPI * kWaves == BC, "whole gather instructions per wavefront");
 
   typedef short i16x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-  struct Loads {
-    u32x4_t k[TPT][4];
-    u32x4_t v[TPT][4];
-  };
+  static __device__ __forceinline__ int swz_k(int r) { return r % 16; }
+  static __device__ __forceinline__ int swz_v(int r) { return 2 * (r % 8); }
+
   // Page ids loaded a tile ahead of their rows, kept as loaded (see MfmaBody::Rows)
   struct Rows {
-    uint32_t page[TPT][4];
-    uint32_t off[TPT][4];   // head * P + slot: row = page * (H_kv * P) + off
+    uint32_t page[NI];
+    uint32_t off[NI];   // head * P + slot: row = page * (H_kv * P) + off
   };
 
-  static __device__ __forceinline__ void task_of(int i, int& qd, int& ch) {
-    const int task = threadIdx.x + i * kWgThreads;
-    qd = task / NCH;
-    ch = task % NCH;
+  static __device__ __forceinline__ int lane_row(int wave, int lane, int n) {
+    return RPI * (NI * wave + n) + lane / NCH;
   }
 
   static __device__ __forceinline__ void load_rows(const RunParams& p, __amdgpu_buffer_rsrc_t ir,
-                                                   const WorkItem& it, int tile, Rows& out) {
+                                                   const WorkItem& it, int tile, int wave, int lane, Rows& out) {
+    const int tau0 = it.kv_begin + tile * BC;
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      int qd, ch;
-      task_of(i, qd, ch);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int tau = it.kv_begin + tile * BC + 4 * qd + j;
-        tau = min(tau, it.kv_end - 1);
-        const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
-        const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-        out.page[i][j] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
-        out.off[i][j] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
-      }
+    for (int n = 0; n < NI; ++n) {
+      const int tau = min(tau0 + lane_row(wave, lane, n), it.kv_end - 1);
+      const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+      const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+      out.page[n] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+      out.off[n] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
     }
   }
 
-  static __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                                 uint32_t rows_per_page, const Rows& rows, Loads& out) {
+  // Gather this lane's rows N0 <= n < N1 of a tile's K and V into a buffer (K at
+  // buf, V at buf + BC * D).
+  template <int N0 = 0, int N1 = NI>
+  static __device__ __forceinline__ void gather(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                                uint32_t rows_per_page, const Rows& rows, uint16_t* buf, int wave,
+                                                int lane) {
+    const int slot = lane % NCH;
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      int qd, ch;
-      task_of(i, qd, ch);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = static_cast<int>(rows.page[i][j] * rows_per_page + rows.off[i][j]);
-        out.k[i][j] = bsr_struct_load_b128(kr, row, ch * 16, 0, 0);
-        out.v[i][j] = bsr_struct_load_b128(vr, row, ch * 16, 0, 0);
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void store_lds(const Loads& in, uint16_t* lk, uint16_t* lv) {
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      int qd, ch;
-      task_of(i, qd, ch);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * qd + j;
-        *reinterpret_cast<u32x4_t*>(lk + r * KPAD + 8 * ch) = in.k[i][j];
-        *reinterpret_cast<u32x4_t*>(lv + r * VPAD + 8 * ch) = in.v[i][j];
-      }
+    for (int n = N0; n < N1; ++n) {
+      const int r = lane_row(wave, lane, n);
+      const int row = static_cast<int>(rows.page[n] * rows_per_page + rows.off[n]);
+      uint16_t* dst = buf + (NI * wave + n) * 512;
+      lds_gather_b128(kr, dst, row, 16 * (slot ^ swz_k(r)));
+      lds_gather_b128(vr, dst + BC * D, row, 16 * (slot ^ swz_v(r)));
     }
   }
 
@@ -130,8 +115,10 @@ struct MfmaBody16 {
       s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
+        // row 16 kb + r16, chunk 4 ks + grp (swz_k(16 kb + r16) == swz_k(r16))
         const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + (16 * kb + r16) * KPAD + 32 * ks + 8 * grp));
+            bf16x8_t,
+            *reinterpret_cast<const u32x4_t*>(lk + (16 * kb + r16) * D + 8 * ((4 * ks + grp) ^ swz_k(r16))));
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], s[kb], 0, 0, 0);
       }
     }
@@ -209,9 +196,10 @@ struct MfmaBody16 {
                                             f32x4_t (&acc)[DB]) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int d = 16 * db + d_off;
-      const i16x4_t lo = read_tr(lv + key_off * VPAD + d);
-      const i16x4_t hi = read_tr(lv + (16 + key_off) * VPAD + d);
+      // chunk (16 db + d_off) / 8 of rows key_off and 16 + key_off (same swizzle)
+      const int at = 8 * ((2 * db + d_off / 8) ^ swz_v(key_off)) + d_off % 8;
+      const i16x4_t lo = read_tr(lv + key_off * D + at);
+      const i16x4_t hi = read_tr(lv + (16 + key_off) * D + at);
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[db], 0, 0, 0);
     }
@@ -258,38 +246,32 @@ struct MfmaBody16 {
     const int ntok = it.kv_end - it.kv_begin;
     const int ntiles = (ntok + BC - 1) / BC;
     const uint32_t rpp = static_cast<uint32_t>(p.h_kv * p.page_size);
-    Rows rows_next;
-    Loads regs;
-    // Two buffers: tile t lives in buffer t % 2; the registers carry tile t + 1
-    // while tile t is computed and go to the other buffer at the next step.
+    Rows rows;
+    // Two buffers: tile t lives in buffer t % 2.  The gather of tile t + 1 and the
+    // page ids of tile t + 2 are issued while tile t is computed and waited for at
+    // the next step.
     if (ntiles > 0) {
-      load_rows(p, irs, it, 0, rows_next);
-      load_kv(krs, vrs, rpp, rows_next, regs);
-      store_lds(regs, lds_h, lds_h + BC * KPAD);
-      if (ntiles > 1) {
-        load_rows(p, irs, it, 1, rows_next);
-        load_kv(krs, vrs, rpp, rows_next, regs);
-        load_rows(p, irs, it, ntiles > 2 ? 2 : 1, rows_next);
-      }
+      load_rows(p, irs, it, 0, wave, lane, rows);
+      gather(krs, vrs, rpp, rows, lds_h, wave, lane);
+      if (ntiles > 1) load_rows(p, irs, it, 1, wave, lane, rows);
     }
     for (int t = 0; t < ntiles; ++t) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
       const uint16_t* lk = lds_h + (t & 1) * STAGE;
-      if (t + 1 < ntiles) {
-        uint16_t* nk = lds_h + ((t + 1) & 1) * STAGE;
-        store_lds(regs, nk, nk + BC * KPAD);
-        if (t + 2 < ntiles) {
-          load_kv(krs, vrs, rpp, rows_next, regs);
-          load_rows(p, irs, it, t + 3 < ntiles ? t + 3 : t + 2, rows_next);
-        }
-      }
+      uint16_t* nb = lds_h + ((t + 1) & 1) * STAGE;
+      if (t + 1 < ntiles) gather<0, NI / 2>(krs, vrs, rpp, rows, nb, wave, lane);
       f32x4_t s[KB];
       qk(lk, qreg, r16, grp, s);
+      if (t + 1 < ntiles) {
+        gather<NI / 2, NI>(krs, vrs, rpp, rows, nb, wave, lane);
+        if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);
+      }
       cap_and_mask(p, it, t, t_local, grp, s);
       bf16x8_t pb;
       const float alpha = softmax(s, c, m_run, l_run, pb);
       rescale(alpha, acc);
-      pv(lk + BC * KPAD, pb, key_off, d_off, acc);
+      pv(lk + BC * D, pb, key_off, d_off, acc);
     }
 
     // result: this lane holds O^T[16 db + 4 grp + i][rho]; the row's sum is spread
