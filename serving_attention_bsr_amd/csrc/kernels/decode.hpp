@@ -88,6 +88,53 @@ struct DecodeBody {
     float l[ROWS];
   };
 
+  // The state of the lane LEVEL lanes away in the ⊕ across lane groups, as a pair
+  // (a, b) to be combined.  Below 16, a rotation by LEVEL within each 16 lanes (the
+  // partner keeps this lane's chunk index lane % LPT; rotations by LPT, 2 LPT, ...
+  // reach all groups of the 16): a = own value, b = the partner's.  At 16 and 32
+  // the lane-half swaps hand both partners the same pair, in lane order.  No LDS.
+  template <int LEVEL>
+  static __device__ __forceinline__ void partner(float x, float& a, float& b) {
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (LEVEL == 32) {
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      a = __uint_as_float(r[0]);
+      b = __uint_as_float(r[1]);
+    } else if constexpr (LEVEL == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      a = __uint_as_float(r[0]);
+      b = __uint_as_float(r[1]);
+    } else {
+      a = x;
+      b = dpp_mov<0x120 + LEVEL>(x);  // row_ror:LEVEL
+    }
+  }
+
+  template <int LEVEL>
+  static __device__ __forceinline__ void merge_groups(State& st) {
+    if constexpr (LEVEL < 64) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        float ma, mb, la, lb;
+        partner<LEVEL>(st.m[r], ma, mb);
+        partner<LEVEL>(st.l[r], la, lb);
+        const float m_new = __builtin_fmaxf(ma, mb);
+        const float m_use = m_new == kNegInf ? 0.0f : m_new;
+        const float fa = fast_exp2(ma - m_use);
+        const float fb = fast_exp2(mb - m_use);
+        st.l[r] = la * fa + lb * fb;
+        st.m[r] = m_new;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float xa, xb;
+          partner<LEVEL>(st.acc[r][e], xa, xb);
+          st.acc[r][e] = xa * fa + xb * fb;
+        }
+      }
+      merge_groups<LEVEL * 2>(st);
+    }
+  }
+
   static __device__ __forceinline__ float dot_row(const uint4 (&q)[NLD], const uint4 (&k)[NLD]) {
     float s = 0.0f;
 #pragma unroll
@@ -266,26 +313,8 @@ struct DecodeBody {
       }
     }
 
-    // ⊕ across the lane groups of this wavefront (lanes differing in bits >= log2(LPT))
-#pragma unroll
-    for (int mask = LPT; mask < 64; mask <<= 1) {
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        const float mo = shfl_xor_f(st.m[r], mask);
-        const float lo = shfl_xor_f(st.l[r], mask);
-        const float m_new = __builtin_fmaxf(st.m[r], mo);
-        const float m_use = m_new == kNegInf ? 0.0f : m_new;
-        const float a_self = fast_exp2(st.m[r] - m_use);
-        const float a_other = fast_exp2(mo - m_use);
-        st.l[r] = st.l[r] * a_self + lo * a_other;
-        st.m[r] = m_new;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float ao = shfl_xor_f(st.acc[r][e], mask);
-          st.acc[r][e] = st.acc[r][e] * a_self + ao * a_other;
-        }
-      }
-    }
+    // ⊕ across the lane groups of this wavefront (lanes with the same lane % LPT)
+    merge_groups<LPT>(st);
 
     // ⊕ across the four wavefronts through LDS: [wave][row][D] accumulators then
     // [wave][row] (m, l)

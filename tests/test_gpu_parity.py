@@ -40,6 +40,10 @@ SWEEP = [
     ("mfma_d128_g8_causal", [33, 200], [40, 200], 16, 2, 128, 2, "bf16", True, 0.0, 0),
     ("mixed_decode_prefill", [1, 50, 1, 3], [500, 120, 77, 3], 32, 8, 128, 4, "bf16", True, 0.0, 16),
     ("mfma_empty_kv_rows", [20, 5], [0, 9], 8, 2, 128, 16, "bf16", False, 0.0, 0),
+    # LDS-direct gather: one-key pages at D = 64, odd page sizes at D = 256, many tiles
+    ("mfma_d64_causal_p1", [70, 130], [200, 130], 8, 2, 64, 1, "bf16", True, 0.0, 0),
+    ("mfma_d256_p5_split", [70, 20], [333, 800], 8, 2, 256, 5, "bf16", False, 0.0, 8),
+    ("mfma_d128_p16_long", [100, 64], [3000, 64], 8, 2, 128, 16, "bf16", True, 0.0, 0),
 ]
 
 
