@@ -102,13 +102,13 @@ struct MfmaBody {
   // Gather this lane's rows N0 <= n < N1 of a tile's K and V into a buffer (K at
   // buf, V at buf + BC * D).  rows_per_page = H_kv * P: pool rows between
   // consecutive pages.
-  template <int N0 = 0, int N1 = NI>
   static __device__ __forceinline__ void gather(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                                 uint32_t rows_per_page, const Rows& rows, uint16_t* buf, int wave,
-                                                int lane) {
+                                                int lane, int n0 = 0, int n1 = NI) {
     const int slot = lane % NCH;
 #pragma unroll
-    for (int n = N0; n < N1; ++n) {
+    for (int n = 0; n < NI; ++n) {
+      if (n < n0 || n >= n1) continue;  // n0, n1 are constants where this is inlined
       const int r = lane_row(wave, lane, n);
       const int row = static_cast<int>(rows.page[n] * rows_per_page + rows.off[n]);
       uint16_t* dst = buf + (NI * wave + n) * 512;
@@ -125,8 +125,12 @@ struct MfmaBody {
   // ---- pieces of one tile step -------------------------------------------------
 
   // S^T = K Q^T for the tile whose K rows start at lk (32-key blocks kb).
+  // hook(h) runs after each half of each block's products (h = 0 .. 2 KB - 1): the
+  // next tile's gather is issued there, a slice at a time, so that its loads
+  // enter the address unit's queue between products instead of in one burst.
+  template <typename Hook>
   static __device__ __forceinline__ void qk(const uint16_t* lk, const bf16x8_t (&qreg)[DK], int col, int half,
-                                            f32x16_t (&s)[KB]) {
+                                            f32x16_t (&s)[KB], Hook&& hook) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -137,6 +141,7 @@ struct MfmaBody {
         const bf16x8_t a = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * D + 8 * ((2 * ks + half) ^ swz_k(col))));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
+        if ((ks + 1) % (DK / 2) == 0) hook(2 * kb + (ks + 1) / (DK / 2) - 1);
       }
     }
   }
@@ -294,15 +299,14 @@ struct MfmaBody {
       __syncthreads();
       const uint16_t* lk = lds_h + (t & 1) * STAGE;
       uint16_t* nb = lds_h + ((t + 1) & 1) * STAGE;
-      // the gather of tile t + 1 is issued in two halves around the S^T products,
-      // so that the workgroups of a CU do not all queue their loads at once
-      if (t + 1 < ntiles) gather<0, NI / 2>(krs, vrs, rpp, rows, nb, wave, lane);
+      // the gather of tile t + 1, a slice after each half block of S^T products
+      const bool more = t + 1 < ntiles;
       f32x16_t s[KB];
-      qk(lk, qreg, col, half, s);
-      if (t + 1 < ntiles) {
-        gather<NI / 2, NI>(krs, vrs, rpp, rows, nb, wave, lane);
-        if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);
-      }
+      qk(lk, qreg, col, half, s, [&](int h) {
+        constexpr int H = 2 * KB;
+        if (more) gather(krs, vrs, rpp, rows, nb, wave, lane, h * NI / H, (h + 1) * NI / H);
+      });
+      if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);
       cap_and_mask(p, it, t, t_local, half, s);
       bf16x8_t pb[KB][2];
       const float alpha = softmax(s, c, m_run, l_run, pb);
