@@ -101,7 +101,35 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
+// The values of this lane and of the lane MASK (16 or 32) lanes away, as a pair in
+// lane order (the same pair on both lanes), by the gfx950 lane-half swaps: no LDS
+// round trip, and both lanes combine the pair in the same order.
+template <int MASK>
+__device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
+  static_assert(MASK == 16 || MASK == 32, "lane-half swaps exchange 16 or 32 lanes apart");
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (MASK == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  }
+}
+template <int MASK>
+__device__ __forceinline__ float pair_max(float x) {
+  float lo, hi;
+  lane_pair<MASK>(x, lo, hi);
+  return __builtin_fmaxf(lo, hi);
+}
+template <int MASK>
+__device__ __forceinline__ float pair_sum(float x) {
+  float lo, hi;
+  lane_pair<MASK>(x, lo, hi);
+  return lo + hi;
+}
 
 // Workspace views.
 __device__ __forceinline__ const PlanHeader* plan_header(const uint8_t* ws) {

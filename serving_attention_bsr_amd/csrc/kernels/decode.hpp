@@ -95,15 +95,8 @@ struct DecodeBody {
   // the lane-half swaps hand both partners the same pair, in lane order.  No LDS.
   template <int LEVEL>
   static __device__ __forceinline__ void partner(float x, float& a, float& b) {
-    const uint32_t u = __float_as_uint(x);
-    if constexpr (LEVEL == 32) {
-      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      a = __uint_as_float(r[0]);
-      b = __uint_as_float(r[1]);
-    } else if constexpr (LEVEL == 16) {
-      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-      a = __uint_as_float(r[0]);
-      b = __uint_as_float(r[1]);
+    if constexpr (LEVEL >= 16) {
+      lane_pair<LEVEL>(x, a, b);
     } else {
       a = x;
       b = dpp_mov<0x120 + LEVEL>(x);  // row_ror:LEVEL

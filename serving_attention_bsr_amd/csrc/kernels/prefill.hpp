@@ -178,7 +178,7 @@ struct MfmaBody {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
-    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32)) * c;
+    mx = pair_max<32>(mx) * c;
     const float m_new = __builtin_fmaxf(m_run, mx);
     const float m_use = m_new == kNegInf ? 0.0f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
@@ -315,7 +315,7 @@ struct MfmaBody {
     }
 
     // result: this lane's column holds O^T[d][rho] for d = 32 db + 8 (r/4) + 4 half + r%4
-    const float l_tot = l_run + shfl_xor_f(l_run, 32);
+    const float l_tot = pair_sum<32>(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse2 = l_tot > 0.0f ? m_run + fast_log2(l_tot) : kNegInf;
     if (row_ok) {

@@ -157,8 +157,7 @@ struct MfmaBody16 {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, s[kb][i]);
-    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32)) * c;
+    mx = pair_max<32>(pair_max<16>(mx)) * c;
     const float m_new = __builtin_fmaxf(m_run, mx);
     const float m_use = m_new == kNegInf ? 0.0f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
@@ -276,8 +275,7 @@ struct MfmaBody16 {
 
     // result: this lane holds O^T[16 db + 4 grp + i][rho]; the row's sum is spread
     // over its four lanes
-    float l_tot = l_run + shfl_xor_f(l_run, 16);
-    l_tot += shfl_xor_f(l_tot, 32);
+    const float l_tot = pair_sum<32>(pair_sum<16>(l_run));
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse2 = l_tot > 0.0f ? m_run + fast_log2(l_tot) : kNegInf;
     if (row_ok) {
