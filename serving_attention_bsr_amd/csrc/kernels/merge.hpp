@@ -32,6 +32,10 @@ struct MergeBody {
   static constexpr int MAX_SLOTS = kMergeMaxGroup * D / 4;                       // float4 slots of a task
   static constexpr int KSLOTS = (MAX_SLOTS + kWgThreads - 1) / kWgThreads;       // slots per thread, at most
   static constexpr int SB = KSLOTS >= 4 ? 2 : (KSLOTS >= 2 ? 4 : 8);            // sources per batch
+  // tasks whose rows need at most one float4 slot per thread (g * D <= 1024) load
+  // this many sources per batch, so one round trip covers a task of up to
+  // FAST_SB * (threads / slots) sources
+  static constexpr int FAST_SB = 16;
   // LDS floats: per-thread group states (m, l, acc) for the cross-group combine
   static constexpr int LDS_FLOATS = kWgThreads * 6;
 
@@ -48,6 +52,16 @@ struct MergeBody {
   // Merge one task (all threads).  The caller has waited for the sources' stamps;
   // states are read with device-scope loads.
   static __device__ void run(const RunParams& p, const MergeTask& t, const MergeSrc* srcs, float* lds) {
+    if (p.group * D <= 4 * kWgThreads)
+      run_slots<1, FAST_SB>(p, t, srcs, lds);
+    else
+      run_slots<KSLOTS, SB>(p, t, srcs, lds);
+  }
+
+  // KS float4 slots per thread, NB sources per batch.
+  template <int KS, int NB>
+  static __device__ __forceinline__ void run_slots(const RunParams& p, const MergeTask& t, const MergeSrc* srcs,
+                                                   float* lds) {
     const int g = p.group;
     const int n = t.src_count;
     const MergeSrc* src = srcs + t.src_begin;
@@ -61,12 +75,12 @@ struct MergeBody {
     const bool active = grp < groups;
 
     // per slot k: running max (base 2), sum of weights, weighted sum of outputs
-    float m[KSLOTS], l[KSLOTS];
-    float4 acc[KSLOTS];
-    int row[KSLOTS], dcol[KSLOTS];
-    bool has[KSLOTS];
+    float m[KS], l[KS];
+    float4 acc[KS];
+    int row[KS], dcol[KS];
+    bool has[KS];
 #pragma unroll
-    for (int k = 0; k < KSLOTS; ++k) {
+    for (int k = 0; k < KS; ++k) {
       const int slot = slot0 + k * kWgThreads;
       has[k] = active && (k == 0 || slots > kWgThreads) && slot < slots;
       row[k] = has[k] ? (slot * 4) / D : 0;
@@ -76,31 +90,37 @@ struct MergeBody {
       acc[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     if (active) {
-      // sources grp, grp + groups, ... in batches of SB loaded together; past the
+      // sources grp, grp + groups, ... in batches of NB loaded together; past the
       // end a batch repeats the group's last source with weight zero
       const int mine = n > grp ? (n - grp + groups - 1) / groups : 0;
-      for (int b = 0; b < mine; b += SB) {
-        float ls[SB][KSLOTS];
-        float4 os[SB][KSLOTS];
-        bool live[SB];
+      for (int b = 0; b < mine; b += NB) {
+        // the batch's partial-state rows first, then all its loads: the load
+        // counter completes in order, so reading a row index between the state
+        // loads would wait for every load before it
+        int prow[NB];
+        bool live[NB];
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
+        for (int j = 0; j < NB; ++j) {
           live[j] = b + j < mine;
-          const int s = grp + groups * min(b + j, mine - 1);
-          const int prow = src[s].partial_row;
+          prow[j] = load_invariant(&src[grp + groups * min(b + j, mine - 1)].partial_row);
+        }
+        float ls[NB][KS];
+        float4 os[NB][KS];
 #pragma unroll
-          for (int k = 0; k < KSLOTS; ++k) {
+        for (int j = 0; j < NB; ++j) {
+#pragma unroll
+          for (int k = 0; k < KS; ++k) {
             if (!has[k]) continue;
-            ls[j][k] = load_dev_f32(pl + prow + row[k]);
-            os[j][k] = load_dev_f32x4(po + static_cast<int64_t>(prow + row[k]) * D + dcol[k]);
+            ls[j][k] = load_dev_f32(pl + prow[j] + row[k]);
+            os[j][k] = load_dev_f32x4(po + static_cast<int64_t>(prow[j] + row[k]) * D + dcol[k]);
           }
         }
 #pragma unroll
-        for (int k = 0; k < KSLOTS; ++k) {
+        for (int k = 0; k < KS; ++k) {
           if (!has[k]) continue;
           float mb = m[k];
 #pragma unroll
-          for (int j = 0; j < SB; ++j)
+          for (int j = 0; j < NB; ++j)
             if (live[j]) mb = __builtin_fmaxf(mb, ls[j][k]);
           const float m_use = mb == kNegInf ? 0.0f : mb;
           const float sc = fast_exp2(m[k] - m_use);
@@ -110,7 +130,7 @@ struct MergeBody {
           acc[k].z *= sc;
           acc[k].w *= sc;
 #pragma unroll
-          for (int j = 0; j < SB; ++j) {
+          for (int j = 0; j < NB; ++j) {
             const float w = live[j] ? fast_exp2(ls[j][k] - m_use) : 0.0f;
             l[k] += w;
             acc[k].x = __builtin_fmaf(w, os[j][k].x, acc[k].x);
@@ -153,7 +173,7 @@ struct MergeBody {
     }
     if (grp == 0) {
 #pragma unroll
-      for (int k = 0; k < KSLOTS; ++k) {
+      for (int k = 0; k < KS; ++k) {
         if (!has[k]) continue;
         const float z = l[k];
         const float inv = z > 0.0f ? 1.0f / z : 0.0f;
