@@ -25,6 +25,18 @@ __device__ __forceinline__ float tanh_exp(float x) {
   return __builtin_copysignf(t, x);
 }
 
+// Lazy reference maximum of the online softmax (base 2) of the MFMA bodies: a
+// row's reference moves only when a tile's maximum exceeds it by more than
+// kLazyMax, so most tiles leave the output accumulator unscaled.  The result is the
+// same: O and the sum are both relative to the reference, and exp2(s - m_ref) is
+// then at most 2^kLazyMax, which the fp32 sums and the bf16 probabilities hold as
+// accurately as values up to 1.  A first finite maximum is always taken
+// (-inf + kLazyMax = -inf).
+constexpr float kLazyMax = 8.0f;
+__device__ __forceinline__ float lazy_max(float m_ref, float tile_max) {
+  return tile_max > m_ref + kLazyMax ? tile_max : m_ref;
+}
+
 // Unsigned division of n < 2^31 by a divisor fixed at set-up (Granlund and
 // Montgomery, "Division by invariant integers using multiplication", 1994).
 __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t magic, int32_t shift) {

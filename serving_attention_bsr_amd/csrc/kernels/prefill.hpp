@@ -169,8 +169,9 @@ struct MfmaBody {
     }
   }
 
-  // Online softmax of one tile: probabilities into the P registers (bf16), running
-  // max and sum updated; returns the factor the accumulator must be scaled by.
+  // Online softmax of one tile: probabilities into the P registers (bf16), the
+  // reference maximum (lazy, see lazy_max) and the sum updated; returns the factor
+  // the accumulator must be scaled by (exactly 1 when the reference stays).
   static __device__ __forceinline__ float softmax(const f32x16_t (&s)[KB], float c, float& m_run, float& l_run,
                                                   bf16x8_t (&pb)[KB][2]) {
     float mx = kNegInf;
@@ -179,9 +180,9 @@ struct MfmaBody {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
     mx = pair_max<32>(mx) * c;
-    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float m_new = lazy_max(m_run, mx);
     const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float alpha = m_new == m_run ? 1.0f : fast_exp2(m_run - m_use);
     m_run = m_new;
     float psum = 0.0f;
 #pragma unroll

@@ -147,9 +147,10 @@ struct MfmaBody16 {
     }
   }
 
-  // Online softmax of one tile; returns the accumulator factor.  m_run is the
-  // row's running max (the same in the row's four lanes), l_run this lane's share
-  // of the running sum.
+  // Online softmax of one tile; returns the accumulator factor (exactly 1 when
+  // the reference stays).  m_run is the row's reference maximum (lazy, see
+  // lazy_max; the same in the row's four lanes), l_run this lane's share of the
+  // running sum.
   static __device__ __forceinline__ float softmax(const f32x4_t (&s)[KB], float c, float& m_run, float& l_run,
                                                   bf16x8_t& pb) {
     float mx = kNegInf;
@@ -158,9 +159,9 @@ struct MfmaBody16 {
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, s[kb][i]);
     mx = pair_max<32>(pair_max<16>(mx)) * c;
-    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float m_new = lazy_max(m_run, mx);
     const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float alpha = m_new == m_run ? 1.0f : fast_exp2(m_run - m_use);
     m_run = m_new;
     float psum = 0.0f;
 #pragma unroll
