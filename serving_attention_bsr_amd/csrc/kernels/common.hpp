@@ -64,12 +64,21 @@ __device__ u32x4_t bsr_struct_load_b128(__amdgpu_buffer_rsrc_t rsrc, int vindex,
     __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
 
 // The same 16-byte row gather written straight into LDS, without passing through
-// registers: lane i of the wavefront lands at lds + 16 i (lds is wave-uniform).
-// Completion is counted by the vector memory counter like any load; the writes are
-// visible to the rest of the workgroup after that counter drains and a barrier.
+// registers: lane i of the wavefront lands at lds + 16 i (lds is wave-uniform;
+// the low 32 bits of a generic pointer into LDS are its LDS address).  Completion
+// is counted by the vector memory counter like any load; the writes are visible
+// to the rest of the workgroup after that counter drains and a barrier, which the
+// callers issue explicitly before a gathered buffer is read.  The load is issued
+// from an asm statement (it writes no register; M0 is set in the same statement):
+// the compiler cannot tell two LDS buffers apart, so for the intrinsic it would
+// wait for every gather in flight (the next tile's, into the other buffer) before
+// any later LDS read it cannot prove independent, such as the transpose reads.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void lds_gather_b128(__amdgpu_buffer_rsrc_t rsrc, void* lds, int vindex, int voffset) {
-  __builtin_amdgcn_struct_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, vindex,
-                                              voffset, 0, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  const i32x2_t va = {vindex, voffset};
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 idxen offen lds" ::"s"(m0), "v"(va), "s"(rsrc)
+               : "memory");
 }
 
 // Element i of a 32-bit array through a raw buffer resource (32-bit offset).

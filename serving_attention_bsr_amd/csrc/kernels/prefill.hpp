@@ -86,16 +86,11 @@ struct MfmaBody {
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
       const int tau = min(tau0 + lane_row(wave, lane, n), it.kv_end - 1);
-      if (p.page_size == 1) {
-        // one key per page: no division
-        out.page[n] = load_u32(ir, it.page_begin + tau);
-        out.off[n] = static_cast<uint32_t>(it.kv_head);
-      } else {
-        const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
-        const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-        out.page[n] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
-        out.off[n] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
-      }
+      // (a page size of 1 gives magic 1, shift 0: the quotient is tau itself)
+      const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+      const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+      out.page[n] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+      out.off[n] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
     }
   }
 
