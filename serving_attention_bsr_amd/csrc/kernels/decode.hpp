@@ -220,28 +220,37 @@ struct DecodeBody {
     }
   }
 
-  // Folded query rows of an item: row r = token (r / g) of the tile, head
-  // kv_head * g + r % g; rows past the item's are zero.
-  static __device__ __forceinline__ void load_q(const RunParams& p, const WorkItem& it, int c,
-                                                uint4 (&q)[ROWS][NLD]) {
+  // Attention of one work item; result in the workgroup-combined (O, log2-sum-exp)
+  // handed to `emit(row, d_pair, o0, o1, lse2)`.
+  template <typename Emit>
+  static __device__ void run(const RunParams& p, const WorkItem& it, float* lds, Emit&& emit) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps loops scalar
+    const int c = lane % LPT;
+    const int grp = lane / LPT;
     const int g = p.group;
     const int rows_valid = it.qo_count * g;
-    const uint8_t* qb = static_cast<const uint8_t*>(p.q);
+
+    // folded query rows: row r = token (r / g) of the tile, head kv_head * g + r % g
+    uint4 q[ROWS][NLD];
+    {
+      const uint8_t* qb = static_cast<const uint8_t*>(p.q);
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      if (r < rows_valid) {
-        const int64_t qrow = static_cast<int64_t>(it.qo_begin + r / g) * p.h_qo + it.kv_head * g + r % g;
-        const uint8_t* src = qb + qrow * (D * ESZ) + c * 16;
+      for (int r = 0; r < ROWS; ++r) {
+        if (r < rows_valid) {
+          const int64_t qrow = static_cast<int64_t>(it.qo_begin + r / g) * p.h_qo +
+                               it.kv_head * g + r % g;
+          const uint8_t* src = qb + qrow * (D * ESZ) + c * 16;
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) q[r][j] = *reinterpret_cast<const uint4*>(src + j * (LPT * 16));
-      } else {
+          for (int j = 0; j < NLD; ++j) q[r][j] = *reinterpret_cast<const uint4*>(src + j * (LPT * 16));
+        } else {
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) q[r][j] = make_uint4(0, 0, 0, 0);
+          for (int j = 0; j < NLD; ++j) q[r][j] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
-  }
 
-  static __device__ __forceinline__ void reset(State& st) {
+    State st;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       st.m[r] = kNegInf;
@@ -249,28 +258,59 @@ struct DecodeBody {
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.acc[r][e] = 0.0f;
     }
-  }
 
-  // Steps this wavefront takes for an item: its tiles are wave, wave + 4, ...;
-  // a wavefront with no tile of a short item takes one fully masked step, so every
-  // wavefront of the workgroup meets every item's combine; an item without keys
-  // takes none.
-  static __device__ __forceinline__ int steps_of(const WorkItem& it, int wave) {
+    // Tiles wave, wave + 4, ... of the item; local tile j of this wavefront.
+    // Pipeline (issue order is what the in-order load counter sees): step j
+    // issues the page ids of tile j+3, then K/V of tile j+2 (its ids arrived a
+    // step ago, and were issued before K/V of tile j+1, so waiting for them
+    // leaves tile j+1 in flight), then computes tile j.  The loop starts at
+    // j = -3 with every key masked while j < 0, so every load is issued and
+    // consumed by the one loop body on every path (a separate prologue, or a
+    // branch around the arithmetic, would leave loads pending into registers
+    // the loop head reuses and force a full wait there).  The id buffers start
+    // at the row of the chunk's first key, and loads past the end are clamped to
+    // its last key, so every load is in bounds and no load sits behind a branch.
+    const __amdgpu_buffer_rsrc_t krs = row_rsrc(p.k_pool, D * ESZ);
+    const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, D * ESZ);
+    const __amdgpu_buffer_rsrc_t irs = row_rsrc(p.kv_indices, 0);
     const int ntok = it.kv_end - it.kv_begin;
-    if (ntok <= 0) return 0;
     const int ntiles = (ntok + TILE - 1) / TILE;
-    return ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 1;
-  }
+    const int nt_w = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+    if (nt_w > 0) {
+      Pids p0, p1, p2;
+      Kv k0 = {}, k1 = {}, k2 = {};  // warm-up steps read these before any load lands
+      {
+        const uint32_t first = load_u32(irs, it.page_begin + it.kv_begin / p.page_size);
+        const uint32_t row0 = (first * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(it.kv_head)) *
+                                  static_cast<uint32_t>(p.page_size) +
+                              static_cast<uint32_t>(it.kv_begin % p.page_size);
+#pragma unroll
+        for (int i = 0; i < TB; ++i) p2.row[i] = row0;
+      }
+      const int t0 = wave;
+      int j = -3;
+      asm volatile("" : "+s"(j));  // keep the warm-up steps inside the loop
+      while (true) {
+        load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p0);
+        load_kv(krs, vrs, c, p2, k2);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k0, st);
+        if (++j >= nt_w) break;
+        load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p1);
+        load_kv(krs, vrs, c, p0, k0);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k1, st);
+        if (++j >= nt_w) break;
+        load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p2);
+        load_kv(krs, vrs, c, p1, k1);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k2, st);
+        if (++j >= nt_w) break;
+      }
+    }
 
-  // End of an item: ⊕ across the lane groups of each wavefront (lanes with the
-  // same lane % LPT), then across the four wavefronts through LDS ([wave][row][D]
-  // accumulators, then [wave][row] (m, l)); the combined (O, log2-sum-exp) goes
-  // to emit(item, row, d_pair, o0, o1, lse2).  Leaves the state reset.
-  template <typename Emit>
-  static __device__ __forceinline__ void finish(const RunParams& p, const WorkItem& it, int c, int grp, int wave,
-                                                State& st, float* lds, Emit&& emit) {
+    // ⊕ across the lane groups of this wavefront (lanes with the same lane % LPT)
     merge_groups<LPT>(st);
-    const int rows_valid = it.qo_count * p.group;
+
+    // ⊕ across the four wavefronts through LDS: [wave][row][D] accumulators then
+    // [wave][row] (m, l)
     float* lacc = lds;
     float* lml = lds + kWaves * ROWS * D;
     if (grp == 0) {
@@ -286,7 +326,6 @@ struct DecodeBody {
         }
       }
     }
-    reset(st);
     __syncthreads();
     for (int idx = threadIdx.x; idx < ROWS * (D / 2); idx += kWgThreads) {
       const int r = idx / (D / 2);
@@ -310,138 +349,12 @@ struct DecodeBody {
       }
       if (lsum > 0.0f) {
         const float inv = 1.0f / lsum;
-        emit(it, r, d, o0 * inv, o1 * inv, big + fast_log2(lsum));
+        emit(r, d, o0 * inv, o1 * inv, big + fast_log2(lsum));
       } else {
-        emit(it, r, d, 0.0f, 0.0f, kNegInf);
+        emit(r, d, 0.0f, 0.0f, kNegInf);
       }
     }
     __syncthreads();
-  }
-
-  // Attention of the work items [ib, ie) of a queue, as one pipeline: the load
-  // side runs three steps ahead of the arithmetic through the queue, so the page
-  // ids and K/V rows of the next item are in flight while this one ends (its
-  // combine and output writes), and the next item's query rows are loaded before
-  // that combine.  Each item's result goes to emit(item, row, d_pair, o0, o1, lse2)
-  // in workgroup-combined form.
-  template <typename Emit>
-  static __device__ void run_queue(const RunParams& p, const WorkItem* items, int ib, int ie, float* lds,
-                                   Emit&& emit) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps loops scalar
-    const int c = lane % LPT;
-    const int grp = lane / LPT;
-
-    State st;
-    reset(st);
-    // compute cursor: item ci (cit), step cj of its cn; items without keys are
-    // finished as they are reached
-    int ci = ib;
-    WorkItem cit;
-    while (true) {
-      if (ci >= ie) return;
-      cit = load_invariant(items + ci);
-      if (cit.kv_end > cit.kv_begin) break;
-      finish(p, cit, c, grp, wave, st, lds, emit);
-      ++ci;
-    }
-    uint4 q[ROWS][NLD];
-    load_q(p, cit, c, q);
-    int cj = 0, cn = steps_of(cit, wave);
-
-    // load cursor: item pi (pit), step pj of its pn; after the last step of the
-    // last item it stays there (its loads repeat valid keys and are never used)
-    int pi = ci, pj = 0, pn = cn;
-    bool pend = false;
-    WorkItem pit = cit;
-    auto advance_load = [&]() {
-      if (pend) return;
-      if (++pj < pn) return;
-      for (int k = pi + 1; k < ie; ++k) {
-        const WorkItem w = load_invariant(items + k);
-        if (w.kv_end > w.kv_begin) {
-          pi = k;
-          pit = w;
-          pj = 0;
-          pn = steps_of(w, wave);
-          return;
-        }
-      }
-      pj = pn - 1;
-      pend = true;
-    };
-    // after the arithmetic of a step: at the end of the current item, load the
-    // next item's queries, finish this item and the keyless ones before the next;
-    // false when the queue is done
-    auto advance_compute = [&]() -> bool {
-      if (++cj < cn) return true;
-      int nx = ci + 1;
-      WorkItem nit = cit;
-      bool more = false;
-      for (; nx < ie; ++nx) {
-        nit = load_invariant(items + nx);
-        if (nit.kv_end > nit.kv_begin) {
-          more = true;
-          break;
-        }
-      }
-      if (more) load_q(p, nit, c, q);  // the combine below does not read q
-      finish(p, cit, c, grp, wave, st, lds, emit);
-      for (int k = ci + 1; k < nx; ++k) finish(p, load_invariant(items + k), c, grp, wave, st, lds, emit);
-      if (!more) return false;
-      ci = nx;
-      cit = nit;
-      cj = 0;
-      cn = steps_of(cit, wave);
-      return true;
-    };
-
-    // Pipeline (issue order is what the in-order load counter sees): step s
-    // issues the page ids of position s+3 of this wavefront's sequence, then K/V
-    // of position s+2 (its ids arrived a step ago, and were issued before K/V of
-    // position s+1, so waiting for them leaves s+1 in flight), then computes
-    // position s.  The loop starts at s = -3 with every key masked while s < 0,
-    // so every load is issued and consumed by the one loop body on every path (a
-    // separate prologue, or a branch around the arithmetic, would leave loads
-    // pending into registers the loop head reuses and force a full wait there).
-    // The warm-up K/V loads read the first key of the first item, and positions
-    // past an item's end are clamped to its last key, so every load is in bounds
-    // and reads finite values.
-    const __amdgpu_buffer_rsrc_t krs = row_rsrc(p.k_pool, D * ESZ);
-    const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, D * ESZ);
-    const __amdgpu_buffer_rsrc_t irs = row_rsrc(p.kv_indices, 0);
-    Pids p0, p1, p2;
-    Kv k0 = {}, k1 = {}, k2 = {};  // warm-up steps read these before any load lands
-    {
-      const uint32_t first = load_u32(irs, cit.page_begin + cit.kv_begin / p.page_size);
-      const uint32_t row0 = (first * static_cast<uint32_t>(p.h_kv) + static_cast<uint32_t>(cit.kv_head)) *
-                                static_cast<uint32_t>(p.page_size) +
-                            static_cast<uint32_t>(cit.kv_begin % p.page_size);
-#pragma unroll
-      for (int i = 0; i < TB; ++i) p2.row[i] = row0;
-    }
-    int s = -3;
-    asm volatile("" : "+s"(s));  // keep the warm-up steps inside the loop
-    while (true) {
-      load_pids(p, irs, pit, wave + pj * kWaves, grp, p0);
-      advance_load();
-      load_kv(krs, vrs, c, p2, k2);
-      step(p, cit, wave + cj * kWaves, grp, s >= 0, q, k0, st);
-      if (s >= 0 && !advance_compute()) break;
-      ++s;
-      load_pids(p, irs, pit, wave + pj * kWaves, grp, p1);
-      advance_load();
-      load_kv(krs, vrs, c, p0, k0);
-      step(p, cit, wave + cj * kWaves, grp, s >= 0, q, k1, st);
-      if (s >= 0 && !advance_compute()) break;
-      ++s;
-      load_pids(p, irs, pit, wave + pj * kWaves, grp, p2);
-      advance_load();
-      load_kv(krs, vrs, c, p1, k1);
-      step(p, cit, wave + cj * kWaves, grp, s >= 0, q, k2, st);
-      if (s >= 0 && !advance_compute()) break;
-      ++s;
-    }
   }
 };
 

@@ -48,27 +48,18 @@ struct PersistentKernel {
       cmax(Merge::LDS_FLOATS, cmax(KIND == kKindMfma ? 0 : Decode::LDS_FLOATS,
                                    KIND == kKindDecode ? 0 : Mfma::LDS_FLOATS));
 
-  // Attention items [ib, ie) of this workgroup's queue.  Consecutive decode items
-  // run as one pipeline (the loads of the next run while this one ends); MFMA
-  // items run one at a time.  emit(item, row, d_pair, o0, o1, lse2).
   template <typename Emit>
-  static __device__ __forceinline__ void attend(const RunParams& p, const WorkItem* items, int32_t ib, int32_t ie,
-                                                float* lds, Emit&& emit) {
+  static __device__ __forceinline__ void attend(const RunParams& p, const WorkItem& it, float* lds,
+                                                Emit&& emit) {
     if constexpr (KIND == kKindDecode) {
-      Decode::run_queue(p, items, ib, ie, lds, emit);
+      Decode::run(p, it, lds, emit);
+    } else if constexpr (KIND == kKindMfma) {
+      Mfma::run(p, it, lds, emit);
     } else {
-      for (int32_t i = ib; i < ie;) {
-        const WorkItem it = load_invariant(items + i);
-        if (KIND == kKindMfma || (it.flags & kItemMfma)) {
-          Mfma::run(p, it, lds, [&](int r, int d, float o0, float o1, float lse2) { emit(it, r, d, o0, o1, lse2); });
-          ++i;
-        } else {
-          int32_t j = i + 1;
-          while (j < ie && !(load_invariant(items + j).flags & kItemMfma)) ++j;
-          if constexpr (KIND == kKindMixed) Decode::run_queue(p, items, i, j, lds, emit);
-          i = j;
-        }
-      }
+      if (it.flags & kItemMfma)
+        Mfma::run(p, it, lds, emit);
+      else
+        Decode::run(p, it, lds, emit);
     }
   }
 };
@@ -111,34 +102,45 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   const int g = p.group;
 
   // ---- attention items -------------------------------------------------------
-  // The queue is read-only during the run: scalar loads.
+  // The queue is read-only during the run: scalar loads, and the next item is
+  // read while this one runs.
   const int32_t* item_ptr = plan_i32(ws, hdr->off_item_ptr);
   const WorkItem* items = reinterpret_cast<const WorkItem*>(ws + hdr->off_items);
   const int32_t ib = load_invariant(item_ptr + wg), ie = load_invariant(item_ptr + wg + 1);
-  float* po = reinterpret_cast<float*>(ws + p.partial_o_off);
-  float* pl = reinterpret_cast<float*>(ws + p.partial_lse_off);
-  auto emit = [&](const WorkItem& it, int r, int d, float o0, float o1, float lse2) {
-    if (it.flags & kItemPartial) {
-      const int64_t row = static_cast<int64_t>(it.partial_row) + r;
-      const uint64_t pair = (static_cast<uint64_t>(__float_as_uint(o1)) << 32) | __float_as_uint(o0);
-      __hip_atomic_store(reinterpret_cast<uint64_t*>(po + row * D + d), pair, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      if (d == 0)
-        __hip_atomic_store(reinterpret_cast<uint32_t*>(pl + row), __float_as_uint(lse2), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const int64_t orow = static_cast<int64_t>(it.qo_begin + r / g) * p.h_qo + it.kv_head * g + r % g;
-      if constexpr (BF16) {
-        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.o) + orow * D + d) = pack_bf16x2(o0, o1);
-      } else {
-        *reinterpret_cast<float2*>(static_cast<float*>(p.o) + orow * D + d) = make_float2(o0, o1);
-      }
-      if (d == 0 && p.lse != nullptr) p.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
-    }
-  };
-  K::attend(p, items, ib, ie, lds, emit);
   bool any_partial = false;
-  for (int32_t i = ib; i < ie; ++i) any_partial |= (load_invariant(&items[i].flags) & kItemPartial) != 0;
+  WorkItem nxt;
+  if (ib < ie) nxt = load_invariant(items + ib);
+  for (int32_t i = ib; i < ie; ++i) {
+    const WorkItem it = nxt;
+    if (i + 1 < ie) nxt = load_invariant(items + i + 1);
+    if (it.flags & kItemPartial) {
+      float* po = reinterpret_cast<float*>(ws + p.partial_o_off);
+      float* pl = reinterpret_cast<float*>(ws + p.partial_lse_off);
+      auto emit = [&](int r, int d, float o0, float o1, float lse2) {
+        const int64_t row = static_cast<int64_t>(it.partial_row) + r;
+        const uint64_t pair = (static_cast<uint64_t>(__float_as_uint(o1)) << 32) | __float_as_uint(o0);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(po + row * D + d), pair, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0)
+          __hip_atomic_store(reinterpret_cast<uint32_t*>(pl + row), __float_as_uint(lse2), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      };
+      K::attend(p, it, lds, emit);
+      any_partial = true;
+    } else {
+      auto emit = [&](int r, int d, float o0, float o1, float lse2) {
+        const int64_t orow =
+            static_cast<int64_t>(it.qo_begin + r / g) * p.h_qo + it.kv_head * g + r % g;
+        if constexpr (BF16) {
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.o) + orow * D + d) = pack_bf16x2(o0, o1);
+        } else {
+          *reinterpret_cast<float2*>(static_cast<float*>(p.o) + orow * D + d) = make_float2(o0, o1);
+        }
+        if (d == 0 && p.lse != nullptr) p.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+      };
+      K::attend(p, it, lds, emit);
+    }
+  }
 
   BSR_STAMP(1);
   // Stamps for the partial states this workgroup wrote: every wavefront waits
