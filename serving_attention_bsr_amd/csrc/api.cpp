@@ -74,7 +74,7 @@ const void* find_kernel(const KernelKey& key, int* wg_per_cu) {
   for (const KernelEntry& e : table) {
     const KernelKey& k = e.key;
     if (k.kind == key.kind && k.bf16 == key.bf16 && k.head_dim == key.head_dim &&
-        k.rows == key.rows && k.cap == key.cap) {
+        k.rows == key.rows && k.cap == key.cap && k.page1 == key.page1) {
       if (wg_per_cu != nullptr) *wg_per_cu = e.wg_per_cu;
       return e.fn;
     }
@@ -183,7 +183,8 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
     const int cus = prop.multiProcessorCount;
     for (int kind = bsr::kKindDecode; kind <= bsr::kKindMixed; ++kind) {
       for (int ri = 0; ri < 2; ++ri) {
-        KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : (ri == 0 ? 4 : 8), cap};
+        KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : (ri == 0 ? 4 : 8), cap,
+                      kind == bsr::kKindMfma && cfg->page_size == 1};
         int preferred = 1;
         const void* fn = bsr::find_kernel(key, &preferred);
         if (fn == nullptr) continue;  // instance not built for this configuration
@@ -303,7 +304,8 @@ static int finish_plan(bsr_attn_t h, std::vector<BlockRow>& rows, int32_t total_
   const void* fn = nullptr;
   if (h->device >= 0) {
     fn = bsr::find_kernel(KernelKey{res.kernel, h->pc.bf16, h->pc.head_dim, rows_key,
-                                    h->cfg.logits_soft_cap > 0.0f});
+                                    h->cfg.logits_soft_cap > 0.0f,
+                                    res.kernel == bsr::kKindMfma && h->pc.page_size == 1});
     if (fn == nullptr)
       return fail(BSR_ERR_UNSUPPORTED, "no kernel built for this plan's kind " + std::to_string(res.kernel));
   }

@@ -40,11 +40,11 @@ inline void add_decode(std::vector<KernelEntry>* out) {
 template <int D>
 constexpr int kMfmaOcc = 2;
 
-template <int D, bool CAP>
+template <int D, bool CAP, bool PAGE1>
 inline void add_mfma(std::vector<KernelEntry>* out) {
-  out->push_back({KernelKey{kKindMfma, true, D, 0, CAP},
+  out->push_back({KernelKey{kKindMfma, true, D, 0, CAP, PAGE1},
                   reinterpret_cast<const void*>(
-                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, kMfmaOcc<D>>),
+                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, kMfmaOcc<D>, PAGE1>),
                   kMfmaOcc<D>});
 }
 
@@ -58,8 +58,11 @@ inline void add_mixed(std::vector<KernelEntry>* out) {
 
 template <int D>
 inline void register_head_dim(std::vector<KernelEntry>* out) {
-  add_mfma<D, false>(out);
-  add_mfma<D, true>(out);
+  add_mfma<D, false, false>(out);
+  add_mfma<D, true, false>(out);
+  // one key per page (radix-tree layout): prefill without the page division
+  add_mfma<D, false, true>(out);
+  add_mfma<D, true, true>(out);
   add_mixed<D, 4, false>(out);
   add_mixed<D, 4, true>(out);
   add_mixed<D, 8, false>(out);

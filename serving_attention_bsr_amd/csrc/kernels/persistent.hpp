@@ -37,12 +37,12 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // KIND selects the attention bodies: decode only, MFMA only (bf16), or both
 // (chosen per work item).
-template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND>
+template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, bool PAGE1>
 struct PersistentKernel {
   static_assert(KIND == kKindDecode || BF16, "the MFMA body is bf16 only");
   using Decode = DecodeBody<D, BF16, ROWS, TB, CAP>;
   // 32 rows per wavefront up to D = 128; 16 rows (two workgroups per CU) at D = 256
-  using Mfma = typename std::conditional<D == 256, MfmaBody16<D, CAP>, MfmaBody<D, CAP>>::type;
+  using Mfma = typename std::conditional<D == 256, MfmaBody16<D, CAP, PAGE1>, MfmaBody<D, CAP, PAGE1>>::type;
   using Merge = MergeBody<D, BF16>;
   static constexpr int LDS_FLOATS =
       cmax(Merge::LDS_FLOATS, cmax(KIND == kKindMfma ? 0 : Decode::LDS_FLOATS,
@@ -78,10 +78,11 @@ struct PersistentKernel {
   } while (0)
 #endif
 
-// OCC: workgroups per CU the register allocation must allow.
-template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, int OCC>
+// OCC: workgroups per CU the register allocation must allow.  PAGE1: the pool has
+// one key per page (MFMA bodies skip the page division).
+template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, int OCC, bool PAGE1 = false>
 __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunParams p) {
-  using K = PersistentKernel<D, BF16, ROWS, TB, CAP, KIND>;
+  using K = PersistentKernel<D, BF16, ROWS, TB, CAP, KIND, PAGE1>;
   __shared__ float lds[K::LDS_FLOATS];
   uint8_t* ws = p.ws;
   // the whole header in one read (its fields are uniform; the empty asm keeps the

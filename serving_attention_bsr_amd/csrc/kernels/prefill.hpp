@@ -39,7 +39,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-template <int D, bool CAP>
+// PAGE1: every page holds one key (page size 1, the radix-tree layout), so a key's
+// page is its own position and no division is needed.
+template <int D, bool CAP, bool PAGE1 = false>
 struct MfmaBody {
   static constexpr int BR = 128;           // folded rows per item
   static constexpr int BC = 64;            // keys per tile
@@ -86,11 +88,15 @@ struct MfmaBody {
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
       const int tau = min(tau0 + lane_row(wave, lane, n), it.kv_end - 1);
-      // (a page size of 1 gives magic 1, shift 0: the quotient is tau itself)
-      const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
-      const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-      out.page[n] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
-      out.off[n] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
+      if constexpr (PAGE1) {
+        out.page[n] = load_u32(ir, it.page_begin + tau);
+        out.off[n] = static_cast<uint32_t>(it.kv_head);
+      } else {
+        const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+        const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+        out.page[n] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+        out.off[n] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
+      }
     }
   }
 
@@ -287,14 +293,13 @@ struct MfmaBody {
       gather(krs, vrs, rpp, rows, lds_h, wave, lane);
       if (ntiles > 1) load_rows(p, irs, it, 1, wave, lane, rows);
     }
-    for (int t = 0; t < ntiles; ++t) {
+    // One tile step: lk is the buffer holding tile t, nb the other one.
+    auto tile = [&](int t, const uint16_t* lk, uint16_t* nb) {
       // this wavefront's gather of tile t (and the ids of tile t + 1) has landed;
       // after the barrier every wavefront's has, and every wavefront is done with
       // tile t - 1, whose buffer now takes tile t + 1
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-      const uint16_t* lk = lds_h + (t & 1) * STAGE;
-      uint16_t* nb = lds_h + ((t + 1) & 1) * STAGE;
       // the gather of tile t + 1, a slice after each half block of S^T products
       const bool more = t + 1 < ntiles;
       f32x16_t s[KB];
@@ -308,6 +313,12 @@ struct MfmaBody {
       const float alpha = softmax(s, c, m_run, l_run, pb);
       rescale(alpha, acc);
       pv(lk + BC * D, pb, key_off, d_off, acc);
+    };
+    // tiles in pairs, so that each step's buffers sit at fixed LDS offsets (the
+    // reads then take them as immediate offsets instead of per-tile address math)
+    for (int t = 0; t < ntiles; t += 2) {
+      tile(t, lds_h, lds_h + STAGE);
+      if (t + 1 < ntiles) tile(t + 1, lds_h + STAGE, lds_h);
     }
 
     // result: this lane's column holds O^T[d][rho] for d = 32 db + 8 (r/4) + 4 half + r%4

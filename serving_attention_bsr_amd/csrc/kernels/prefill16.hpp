@@ -34,7 +34,8 @@ namespace bsr {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int D, bool CAP>
+// PAGE1: every page holds one key, so a key's page is its own position.
+template <int D, bool CAP, bool PAGE1 = false>
 struct MfmaBody16 {
   static constexpr int BR = 64;            // folded rows per item
   static constexpr int BC = 32;            // keys per tile
@@ -79,10 +80,15 @@ struct MfmaBody16 {
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
       const int tau = min(tau0 + lane_row(wave, lane, n), it.kv_end - 1);
-      const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
-      const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
-      out.page[n] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
-      out.off[n] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
+      if constexpr (PAGE1) {
+        out.page[n] = load_u32(ir, it.page_begin + tau);
+        out.off[n] = static_cast<uint32_t>(it.kv_head);
+      } else {
+        const uint32_t pl = div_magic(static_cast<uint32_t>(tau), p.page_magic, p.page_shift);
+        const uint32_t slot = static_cast<uint32_t>(tau) - pl * static_cast<uint32_t>(p.page_size);
+        out.page[n] = load_u32(ir, it.page_begin + static_cast<int32_t>(pl));
+        out.off[n] = static_cast<uint32_t>(it.kv_head * p.page_size) + slot;
+      }
     }
   }
 
@@ -255,11 +261,10 @@ struct MfmaBody16 {
       gather(krs, vrs, rpp, rows, lds_h, wave, lane);
       if (ntiles > 1) load_rows(p, irs, it, 1, wave, lane, rows);
     }
-    for (int t = 0; t < ntiles; ++t) {
+    // One tile step: lk is the buffer holding tile t, nb the other one.
+    auto tile = [&](int t, const uint16_t* lk, uint16_t* nb) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-      const uint16_t* lk = lds_h + (t & 1) * STAGE;
-      uint16_t* nb = lds_h + ((t + 1) & 1) * STAGE;
       if (t + 1 < ntiles) gather<0, NI / 2>(krs, vrs, rpp, rows, nb, wave, lane);
       f32x4_t s[KB];
       qk(lk, qreg, r16, grp, s);
@@ -272,6 +277,11 @@ struct MfmaBody16 {
       const float alpha = softmax(s, c, m_run, l_run, pb);
       rescale(alpha, acc);
       pv(lk + BC * D, pb, key_off, d_off, acc);
+    };
+    // tiles in pairs: fixed buffer offsets for each step's LDS reads
+    for (int t = 0; t < ntiles; t += 2) {
+      tile(t, lds_h, lds_h + STAGE);
+      if (t + 1 < ntiles) tile(t + 1, lds_h + STAGE, lds_h);
     }
 
     // result: this lane holds O^T[16 db + 4 grp + i][rho]; the row's sum is spread

@@ -35,6 +35,7 @@ struct KernelKey {
   int head_dim;
   int rows;  // decode-body folded rows (0 when the kernel has no decode body)
   bool cap;
+  bool page1 = false;  // instance specialised for one key per page (MFMA kind only)
 };
 
 // Host stub of the matching persistent kernel, or null if not built; the

@@ -44,6 +44,9 @@ SWEEP = [
     ("mfma_d64_causal_p1", [70, 130], [200, 130], 8, 2, 64, 1, "bf16", True, 0.0, 0),
     ("mfma_d256_p5_split", [70, 20], [333, 800], 8, 2, 256, 5, "bf16", False, 0.0, 8),
     ("mfma_d128_p16_long", [100, 64], [3000, 64], 8, 2, 128, 16, "bf16", True, 0.0, 0),
+    # one-key-page instances with the soft-cap (odd and even tile counts)
+    ("mfma_d128_p1_cap", [60, 200], [60, 900], 16, 4, 128, 1, "bf16", False, 30.0, 0),
+    ("mfma_d256_p1_cap_split", [70, 9], [500, 9], 8, 2, 256, 1, "bf16", True, 15.0, 8),
 ]
 
 
