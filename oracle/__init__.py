@@ -14,3 +14,4 @@ from .attention import (  # noqa: F401
     merge_state,
     merge_states,
 )
+from .append import append_paged_kv, append_slots  # noqa: F401
