@@ -33,7 +33,10 @@ METRIC = "paged decode attn HBM TB/s (% peak) + ragged prefill TFLOPS (% MFMA pe
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 HEADLINE = "batch_decode"
-ALL = ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill", "shared_prefix_composable"]
+ALL = ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill", "shared_prefix_composable",
+       "append_kv_prefill"]
+# writing the new K/V rows of a workload into its paged cache (not an attention run)
+APPEND = {"append_kv_prefill": "ragged_causal_prefill"}
 
 
 def kernel_source_hash():
@@ -212,6 +215,44 @@ def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
     return out, (w, h)
 
 
+def bench_append(name, steps, warmup, flush, mode="read"):
+    """bsr_attn_append_kv over a workload's new tokens: their K/V rows ([sum l_qo,
+    H_kv, D]) go to the last positions of each request in its page table.  Bound by
+    HBM: every row is read once and written once."""
+    import torch
+
+    from serving_attention_bsr_amd import lib
+    from serving_attention_bsr_amd import workloads as W
+
+    src = APPEND[name]
+    print(f"[bench] {name}: building inputs ({src} page table)", file=sys.stderr, flush=True)
+    w = W.named(src)
+    dev = torch.device("cuda:0")
+    k_pool, v_pool = w.k_pool.to(dev), w.v_pool.to(dev)
+    total_new = int(w.qo_indptr[-1])
+    g = torch.Generator(device=dev).manual_seed(7)
+    shape = (total_new, w.num_kv_heads, w.head_dim)
+    k_new = torch.randn(shape, generator=g, device=dev).to(k_pool.dtype)
+    v_new = torch.randn(shape, generator=g, device=dev).to(k_pool.dtype)
+    idx = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+           for a in (w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len)]
+    elt = k_pool.element_size()
+    row_bytes = total_new * w.num_kv_heads * w.head_dim * elt
+    work_bytes = 2 * 2 * row_bytes + 4 * (len(w.qo_indptr) + 2 * len(w.kv_indptr) + total_new)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lib.append_kv(k_new, v_new, *idx, k_pool, v_pool)
+
+    times, wall = timed_steps(step, steps, warmup, stream, flush, mode)
+    med = float(np.median(times))
+    gbs = work_bytes / (med * 1e-3) / 1e9
+    return dict(workload=name, dtype=w.dtype, rows=total_new * w.num_kv_heads, bytes=work_bytes,
+                ms_median=med, ms_min=float(times.min()), wall_s=wall, hbm_GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)), None
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The oracle as it stands, on the full workload, repeated for about budget_s."""
     import threadpoolctl
@@ -276,8 +317,11 @@ def main():
     results = {}
     keep = {}
     for name in names:
-        r, ctx = bench_workload(name, args.steps, args.warmup, flush, graph=not args.no_graph,
-                                nwg=args.num_workgroups, mode=args.flush)
+        if name in APPEND:
+            r, ctx = bench_append(name, args.steps, args.warmup, flush, mode=args.flush)
+        else:
+            r, ctx = bench_workload(name, args.steps, args.warmup, flush, graph=not args.no_graph,
+                                    nwg=args.num_workgroups, mode=args.flush)
         results[name] = r
         print(f"[bench] {name}: {json.dumps({k: v for k, v in r.items() if k != 'plan'})}", file=sys.stderr, flush=True)
         if name == HEADLINE:

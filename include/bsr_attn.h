@@ -194,6 +194,27 @@ int bsr_attn_merge_states(const float* o_a, const float* lse_a, const float* o_b
                           const float* lse_b, float* o, float* lse, int64_t rows,
                           int32_t head_dim, void* stream);
 
+/* Write new K/V rows into the paged cache (Core mechanism 1, paper section
+ * 3.1.1: new K/V rows are packed like the queries, then written into the BSR
+ * cache).  k_new, v_new: [total_new, H_kv, D] in dtype, rows packed by
+ * append_indptr (int32 [batch + 1], like qo_indptr).  The page table
+ * (kv_indptr, kv_indices, last_page_len; int32, as for bsr_attn_run) describes
+ * each request's KV AFTER the write: the n_r new rows of request r become its
+ * last n_r tokens, row j at position tau = l_kv - n_r + j, i.e. slot tau % P of
+ * page kv_indices[kv_indptr[r] + tau / P] in every head plane of k_pool / v_pool
+ * ([num_pages, H_kv, P, D], dtype).  Rows without a position (n_r > l_kv) and
+ * rows whose page id lies outside [0, num_pages) are not written; nothing else in
+ * the pools changes.  All arrays are device memory owned by the caller.  No
+ * allocation, no synchronisation: asynchronous on `stream` and capturable.
+ * Returns BSR_ERR_INVALID_ARG for negative sizes, null pointers or an unknown
+ * dtype, BSR_ERR_UNSUPPORTED when D times the element size is not a multiple of
+ * 16 bytes. */
+int bsr_attn_append_kv(const void* k_new, const void* v_new, const int32_t* append_indptr,
+                       const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* last_page_len, int32_t batch, int64_t total_new,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t dtype,
+                       void* k_pool, void* v_pool, int64_t num_pages, void* stream);
+
 void bsr_attn_destroy(bsr_attn_t h);
 const char* bsr_attn_last_error(void);
 int bsr_attn_abi_version(void);

@@ -493,6 +493,32 @@ int bsr_attn_merge_states(const float* o_a, const float* lse_a, const float* o_b
   return BSR_OK;
 }
 
+extern int bsr_launch_append_kv(const void*, const void*, const int32_t*, const int32_t*, const int32_t*,
+                                const int32_t*, int32_t, int64_t, int32_t, int32_t, int32_t, int64_t, void*, void*,
+                                hipStream_t);
+
+int bsr_attn_append_kv(const void* k_new, const void* v_new, const int32_t* append_indptr, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, const int32_t* last_page_len, int32_t batch, int64_t total_new,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t dtype, void* k_pool,
+                       void* v_pool, int64_t num_pages, void* stream) {
+  if (batch < 0 || total_new < 0 || num_pages < 0)
+    return fail(BSR_ERR_INVALID_ARG, "batch, total_new and num_pages must be >= 0");
+  if (num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0)
+    return fail(BSR_ERR_INVALID_ARG, "num_kv_heads, head_dim and page_size must be > 0");
+  if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16) return fail(BSR_ERR_INVALID_ARG, "dtype must be F32 or BF16");
+  const int64_t row_bytes = int64_t(head_dim) * (dtype == BSR_DTYPE_F32 ? 4 : 2);
+  if (row_bytes % 16 != 0) return fail(BSR_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16 bytes");
+  if (total_new == 0 || batch == 0) return BSR_OK;
+  if (k_new == nullptr || v_new == nullptr || append_indptr == nullptr || kv_indptr == nullptr ||
+      kv_indices == nullptr || last_page_len == nullptr || k_pool == nullptr || v_pool == nullptr)
+    return fail(BSR_ERR_INVALID_ARG, "null device pointer");
+  if (bsr_launch_append_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, last_page_len, batch, total_new,
+                           num_kv_heads, static_cast<int32_t>(row_bytes), page_size, num_pages, k_pool, v_pool,
+                           static_cast<hipStream_t>(stream)) != 0)
+    return fail(BSR_ERR_HIP, "append_kv launch failed");
+  return BSR_OK;
+}
+
 void bsr_attn_destroy(bsr_attn_t h) {
   if (h == nullptr) return;
   if (h->upload_done != nullptr) {

@@ -42,6 +42,7 @@ EXPORTED = [
     "bsr_attn_run",
     "bsr_attn_check",
     "bsr_attn_merge_states",
+    "bsr_attn_append_kv",
     "bsr_attn_destroy",
 ]
 
@@ -131,6 +132,8 @@ def load():
     lib.bsr_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, f32p, vp, vp]
     lib.bsr_attn_check.argtypes = [vp, vp, vp]
     lib.bsr_attn_merge_states.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p, c_i64, c_i32, vp]
+    lib.bsr_attn_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, vp, vp,
+                                       c_i64, vp]
     lib.bsr_attn_destroy.argtypes = [vp]
     lib.bsr_attn_destroy.restype = None
     for name in EXPORTED:
@@ -222,6 +225,13 @@ def bsr_attn_check(h, workspace, stream):
 
 def bsr_attn_merge_states(o_a, lse_a, o_b, lse_b, o, lse, rows, head_dim, stream):
     _check(load().bsr_attn_merge_states(o_a, lse_a, o_b, lse_b, o, lse, rows, head_dim, stream))
+
+
+def bsr_attn_append_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, last_page_len, batch, total_new,
+                       num_kv_heads, head_dim, page_size, dtype, k_pool, v_pool, num_pages, stream):
+    _check(load().bsr_attn_append_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, last_page_len, batch,
+                                     total_new, num_kv_heads, head_dim, page_size, dtype, k_pool, v_pool, num_pages,
+                                     stream))
 
 
 def bsr_attn_destroy(h):
@@ -366,3 +376,36 @@ def merge_states(o_a, lse_a, o_b, lse_b, o=None, lse=None):
         _stream_ptr(torch.cuda.current_stream(o_a.device)),
     )
     return o, lse
+
+
+def append_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, last_page_len, k_pool, v_pool):
+    """Write new K/V rows ([total_new, H_kv, D]) into the paged pools ([num_pages, H_kv, P, D])
+    in place; the index arrays are int32 tensors on the pools' device (see bsr_attn_append_kv)."""
+    import torch
+
+    for t in (k_new, v_new, k_pool, v_pool, append_indptr, kv_indptr, kv_indices, last_page_len):
+        if not t.is_contiguous():
+            raise ValueError("append_kv needs contiguous tensors")
+    for t in (append_indptr, kv_indptr, kv_indices, last_page_len):
+        if t.dtype != torch.int32:
+            raise ValueError("index arrays must be int32")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != v_pool.dtype or k_pool.dtype != v_pool.dtype:
+        raise ValueError("new rows and pools must share one dtype")
+    if k_pool.dtype == torch.bfloat16:
+        dtype = BSR_DTYPE_BF16
+    elif k_pool.dtype == torch.float32:
+        dtype = BSR_DTYPE_F32
+    else:
+        raise ValueError("dtype must be float32 or bfloat16")
+    num_pages, h_kv, page_size, d = k_pool.shape
+    total_new = k_new.shape[0]
+    if tuple(k_new.shape) != (total_new, h_kv, d) or tuple(v_new.shape) != (total_new, h_kv, d):
+        raise ValueError("k_new / v_new must be [total_new, H_kv, D] matching the pools")
+    if tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("K and V pools differ in shape")
+    batch = append_indptr.numel() - 1
+    bsr_attn_append_kv(
+        _dptr(k_new), _dptr(v_new), _dptr(append_indptr), _dptr(kv_indptr), _dptr(kv_indices), _dptr(last_page_len),
+        batch, total_new, h_kv, d, page_size, dtype, _dptr(k_pool), _dptr(v_pool), num_pages,
+        _stream_ptr(torch.cuda.current_stream(k_pool.device)),
+    )
