@@ -74,7 +74,8 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kv_kernel(
 
 }  // namespace bsr
 
-// Grid: up to 2048 workgroups of 4 wavefronts, each wavefront a contiguous range
+// Grid: up to 16384 workgroups of 4 wavefronts (one token per wavefront up to
+// 64k new tokens: the more rows in flight the better), each a contiguous range
 // of new tokens.
 extern "C" int bsr_launch_append_kv(const void* k_new, const void* v_new, const int32_t* append_indptr,
                                      const int32_t* kv_indptr, const int32_t* kv_indices,
@@ -82,7 +83,7 @@ extern "C" int bsr_launch_append_kv(const void* k_new, const void* v_new, const 
                                      int32_t h_kv, int32_t row_bytes, int32_t page_size, int64_t num_pages,
                                      void* k_pool, void* v_pool, hipStream_t s) {
   if (total_new == 0 || batch == 0) return 0;
-  const int64_t max_waves = 2048LL * bsr::kAppendWaves;
+  const int64_t max_waves = 16384LL * bsr::kAppendWaves;
   const int64_t per_wave = (total_new + max_waves - 1) / max_waves;
   const int64_t waves = (total_new + per_wave - 1) / per_wave;
   const int64_t blocks = (waves + bsr::kAppendWaves - 1) / bsr::kAppendWaves;

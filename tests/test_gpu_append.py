@@ -4,7 +4,8 @@ against the CPU oracle, bit for bit (pure indexing).
 Cases: decode appends (one row per request), whole-request prefill appends with
 one key per page, a ragged mix with an empty request and a request with more new
 rows than positions, D = 256 with an odd page size, a long prefill whose rows
-cross requests inside one wavefront's range, and page ids outside the pool
+cross requests inside one wavefront's range (more rows than wavefronts), and
+page ids outside the pool
 (those rows must not be written).  Pools start with random values everywhere, so
 any write outside the expected slots shows up.
 """
@@ -24,6 +25,9 @@ CASES = [
     ("d256_p5", [40, 41], [17, 1], 2, 256, 5, "bf16", 4),
     ("long_prefill_p16", [1000, 4000, 2500, 3100, 1, 2999, 3500, 2900], [1000, 4000, 2500, 3100, 1, 2999, 3500, 2900],
      8, 128, 16, "bf16", 5),
+    # more new rows than the grid has wavefronts (65536): each wavefront walks two
+    # tokens, across request boundaries
+    ("many_tokens_h1", [30000, 25001, 19999], [30000, 25001, 19999], 1, 64, 16, "bf16", 6),
 ]
 
 
