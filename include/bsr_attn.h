@@ -109,7 +109,11 @@ typedef struct bsr_attn_config {
                               to one of a decode work item, in sixteenths; used when one
                               grid runs both bodies (composed formats, mixed batches);
                               0 selects the measured default for the head dim */
-  int32_t reserved[1];     /* must be 0 */
+  int32_t slot2_speed;     /* in a grid of two workgroups per CU (MFMA tile body), the
+                              rate of each CU's second workgroup relative to its first,
+                              in sixteenths; the planner balances their loads in time
+                              (Core mechanism 6 balances in cost).  0 selects the
+                              measured default, 16 treats them as equal */
 } bsr_attn_config;
 
 /* One BSR sub-matrix for bsr_attn_plan_composable().  Arrays are host memory. */

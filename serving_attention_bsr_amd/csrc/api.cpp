@@ -24,6 +24,10 @@ using bsr::KernelKey;
 using bsr::PlanConfig;
 using bsr::PlanResult;
 
+// Default rate of the second workgroup of a CU in the two-per-CU MFMA grid, in
+// sixteenths of the first's (from a sweep on MI355X; see the planner).
+constexpr int32_t kSlot2Speed16 = 11;
+
 namespace {
 
 thread_local std::string g_error;
@@ -87,6 +91,7 @@ const void* find_kernel(const KernelKey& key, int* wg_per_cu) {
 struct bsr_attn {
   bsr_attn_config cfg;
   int device = -1;
+  int cus = 0;  // compute units of the device (0 for host-only handles)
   PlanConfig pc;
   int32_t num_wg[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};  // [kind][decode rows 4/8]
   int64_t plan_capacity = 0;
@@ -122,11 +127,10 @@ int validate_config(const bsr_attn_config* c) {
     return fail(BSR_ERR_INVALID_ARG, "max_batch, max_total_qo and max_total_kv must be positive");
   if (c->max_total_kv >= (int64_t(1) << 40)) return fail(BSR_ERR_INVALID_ARG, "max_total_kv too large");
   if (c->num_workgroups < 0 || c->cost_alpha < 0 || c->cost_beta < 0 || c->min_kv_chunk < 0 ||
-      c->max_partial_rows < 0 || c->cost_mfma < 0)
+      c->max_partial_rows < 0 || c->cost_mfma < 0 || c->slot2_speed < 0)
     return fail(BSR_ERR_INVALID_ARG, "negative tuning parameter");
   if (c->cost_mfma > 16 * 256) return fail(BSR_ERR_INVALID_ARG, "cost_mfma too large");
-  for (int32_t r : c->reserved)
-    if (r != 0) return fail(BSR_ERR_INVALID_ARG, "reserved fields must be zero");
+  if (c->slot2_speed > 64) return fail(BSR_ERR_INVALID_ARG, "slot2_speed too large");
   return BSR_OK;
 }
 
@@ -181,6 +185,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
       return fail(BSR_ERR_UNSUPPORTED, std::string("kernels are built for gfx950, device is ") + prop.gcnArchName);
     }
     const int cus = prop.multiProcessorCount;
+    h->cus = cus;
     for (int kind = bsr::kKindDecode; kind <= bsr::kKindMixed; ++kind) {
       for (int ri = 0; ri < 2; ++ri) {
         KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : (ri == 0 ? 4 : 8), cap,
@@ -233,6 +238,8 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   // mixed grid runs fastest once MFMA pieces get workgroups of their own, which
   // every weight from 10x up gives; 12x is used.
   pc.mfma_w16 = cfg->cost_mfma > 0 ? cfg->cost_mfma : 192;
+  pc.cus = h->cus;
+  pc.slot2_speed16 = cfg->slot2_speed > 0 ? cfg->slot2_speed : kSlot2Speed16;
   pc.max_batch = cfg->max_batch;
   pc.max_total_qo = cfg->max_total_qo;
   pc.max_total_kv = cfg->max_total_kv;

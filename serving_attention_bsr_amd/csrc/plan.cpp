@@ -73,28 +73,56 @@ struct Item {
   int32_t nchunks;
 };
 
-// Least-loaded assignment; returns the workgroup of each entry (indexed like costs).
-void assign_longest_first(const std::vector<int64_t>& costs, std::vector<int64_t>* load,
-                          std::vector<int32_t>* owner, std::vector<int32_t>* order) {
+// Longest-first assignment: each entry, longest first, goes to the workgroup where
+// it would finish first, i.e. the least-loaded one when all workgroups run at the
+// same speed.  speed16[w] is workgroup w's speed in sixteenths (a workgroup of
+// speed s finishes a cost c in 16 c / s); workgroups of one speed form one
+// min-heap on (load, id), and the heads of the heaps are compared.  Returns the
+// workgroup of each entry (indexed like costs).
+void assign_longest_first(const std::vector<int64_t>& costs, const std::vector<int32_t>& speed16,
+                          std::vector<int64_t>* load, std::vector<int32_t>* owner, std::vector<int32_t>* order) {
   const int32_t n = static_cast<int32_t>(costs.size());
   order->resize(n);
   for (int32_t i = 0; i < n; ++i) (*order)[i] = i;
   std::stable_sort(order->begin(), order->end(),
                    [&](int32_t a, int32_t b) { return costs[a] > costs[b]; });
   using Slot = std::pair<int64_t, int32_t>;  // (load, workgroup)
-  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
-  for (int32_t w = 0; w < static_cast<int32_t>(load->size()); ++w) heap.push({(*load)[w], w});
+  using Heap = std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>>;
+  std::vector<int32_t> speeds;  // distinct speeds, in first-seen order
+  std::vector<Heap> heaps;
+  for (int32_t w = 0; w < static_cast<int32_t>(load->size()); ++w) {
+    size_t k = 0;
+    while (k < speeds.size() && speeds[k] != speed16[w]) ++k;
+    if (k == speeds.size()) {
+      speeds.push_back(speed16[w]);
+      heaps.emplace_back();
+    }
+    heaps[k].push({(*load)[w], w});
+  }
   owner->assign(n, -1);
-  for (int32_t k = 0; k < n; ++k) {
-    const int32_t i = (*order)[k];
-    Slot s = heap.top();
-    heap.pop();
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t i = (*order)[j];
+    size_t best = 0;
+    int64_t best_f = INT64_MAX;
+    for (size_t k = 0; k < heaps.size(); ++k) {
+      const Slot& top = heaps[k].top();
+      const int64_t f = (top.first + costs[i]) * 16 / speeds[k];
+      if (f < best_f || (f == best_f && top.second < heaps[best].top().second)) {
+        best_f = f;
+        best = k;
+      }
+    }
+    Slot s = heaps[best].top();
+    heaps[best].pop();
     (*owner)[i] = s.second;
     s.first += costs[i];
     (*load)[s.second] = s.first;
-    heap.push(s);
+    heaps[best].push(s);
   }
 }
+
+// Time a workgroup needs for its load, in cost units at speed 16.
+inline int64_t finish_time(int64_t load, int32_t speed16) { return load * 16 / speed16; }
 
 struct Schedule {
   int64_t chunk = 0;
@@ -118,8 +146,8 @@ struct Schedule {
 // minimum chunk), so indivisible short units no longer leave some workgroups
 // over-full.
 int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std::vector<Unit>& units,
-             int64_t chunk, bool fill, int32_t nwg, int32_t total_qo, bool composable, Schedule* out,
-             std::string* err) {
+             int64_t chunk, bool fill, int32_t nwg, const std::vector<int32_t>& speed16, int32_t total_qo,
+             bool composable, Schedule* out, std::string* err) {
   (void)err;
   const int32_t g = cfg.group;
   const int32_t h_kv = cfg.h_kv;
@@ -167,7 +195,7 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
     }
     std::vector<int64_t> costs(items.size());
     for (size_t i = 0; i < items.size(); ++i) costs[i] = items[i].cost;
-    assign_longest_first(costs, &load, &owner, &order);
+    assign_longest_first(costs, speed16, &load, &owner, &order);
   } else {
     std::vector<int32_t> short_u, long_u;
     int64_t total = 0;
@@ -321,12 +349,12 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
     mcosts[i] = cfg.gamma + cfg.beta * static_cast<int64_t>(tasks[i].src_count) * g;
   std::vector<int32_t> mowner, morder;
   out->att_load = load;
-  assign_longest_first(mcosts, &load, &mowner, &morder);
+  assign_longest_first(mcosts, speed16, &load, &mowner, &morder);
   out->makespan = 0;
   out->total = 0;
-  for (int64_t l : load) {
-    out->makespan = std::max(out->makespan, l);
-    out->total += l;
+  for (int32_t w = 0; w < nwg; ++w) {
+    out->makespan = std::max(out->makespan, finish_time(load[w], speed16[w]));
+    out->total += load[w];
   }
   // the longest chunk actually cut (L_kv for the pages' rule; filling may cut more;
   // with weighted units L_kv is not in tokens, so only the pieces count)
@@ -360,7 +388,7 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
 // least-loaded workgroups.  A workgroup without tasks whose attention ends by the
 // task's ready time is always a best choice; among those the least loaded (then
 // lowest id) is taken.
-static void assign_merges(const PlanConfig& cfg, int32_t nwg, Schedule* s) {
+static void assign_merges(const PlanConfig& cfg, int32_t nwg, const std::vector<int32_t>& speed16, Schedule* s) {
   const int32_t g = cfg.group;
   const size_t nt = s->tasks.size();
   std::vector<int64_t> mcosts(nt);
@@ -411,7 +439,7 @@ static void assign_merges(const PlanConfig& cfg, int32_t nwg, Schedule* s) {
   s->total = 0;
   for (int32_t w = 0; w < nwg; ++w) {
     const int64_t l = msum[w] > 0 ? std::max(att[w], mready[w]) + msum[w] : att[w];
-    s->makespan = std::max(s->makespan, l);
+    s->makespan = std::max(s->makespan, finish_time(l, speed16[w]));
     s->total += l;
   }
 }
@@ -466,6 +494,18 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
     *err = "the kernel this plan needs (kind " + std::to_string(kernel) + ") is not built for this handle";
     return BSR_ERR_UNSUPPORTED;
   }
+
+  // Workgroup speeds.  In a grid of two workgroups per CU (the MFMA kernel) the
+  // hardware dispatches workgroups 0 .. #CU-1 first, one per CU, and #CU .. 2 #CU-1
+  // into the second slots; while both run, the older wavefronts win the SIMD's
+  // issue arbitration, so the second workgroup of a CU progresses more slowly and,
+  // with equal loads, finishes its last stretch alone (a per-workgroup timeline of
+  // the ragged causal prefill: 1360 us for the first slots, 1720 us for the
+  // second).  Loads are then balanced in time: a second-slot workgroup runs at
+  // slot2_speed16 / 16 of a first-slot one.
+  std::vector<int32_t> speed16(nwg, 16);
+  if (kernel == kKindMfma && cfg.cus > 0 && nwg == 2 * cfg.cus && cfg.slot2_speed16 > 0)
+    for (int32_t w = cfg.cus; w < nwg; ++w) speed16[w] = cfg.slot2_speed16;
 
   // ---- 2. work units ---------------------------------------------------------
   std::vector<Unit> units;
@@ -525,14 +565,14 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
     if (!fill && chunk == last_chunk) continue;
     last_chunk = chunk;
     Schedule cand;
-    int rc = schedule(cfg, rows, units, chunk, fill, nwg, total_qo, composable, &cand, err);
+    int rc = schedule(cfg, rows, units, chunk, fill, nwg, speed16, total_qo, composable, &cand, err);
     if (rc != BSR_OK) return rc;
     if (!have || cand.makespan * 100 < best.makespan * 97) {
       best = std::move(cand);
       have = true;
     }
   }
-  assign_merges(cfg, nwg, &best);
+  assign_merges(cfg, nwg, speed16, &best);
   if (best.partial_rows > cfg.max_partial_rows) {
     *err = "plan needs " + std::to_string(best.partial_rows) + " partial rows, capacity is " +
            std::to_string(cfg.max_partial_rows);

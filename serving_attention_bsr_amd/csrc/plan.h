@@ -27,6 +27,10 @@ struct PlanConfig {
   // cost of one KV token of an MFMA item in a mixed grid, in sixteenths of a
   // decode item's token (16 = equal)
   int32_t mfma_w16 = 16;
+  // CUs of the device (0 for host-only handles) and the speed of the second
+  // workgroup of each CU in a two-per-CU MFMA grid, in sixteenths of the first's
+  int32_t cus = 0;
+  int32_t slot2_speed16 = 16;
   // capacities (plan rejected beyond them)
   int32_t max_batch = 0, max_total_qo = 0;
   int64_t max_total_kv = 0;

@@ -73,7 +73,7 @@ class bsr_attn_config(ctypes.Structure):
         ("max_partial_rows", ctypes.c_int32),
         ("cost_item", ctypes.c_int32),
         ("cost_mfma", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 1),
+        ("slot2_speed", ctypes.c_int32),
     ]
 
 
@@ -270,6 +270,7 @@ class BsrAttention:
         max_partial_rows: int = 0,
         cost_item: int = 0,
         cost_mfma: int = 0,
+        slot2_speed: int = 0,
     ):
         cfg = bsr_attn_config()
         cfg.num_qo_heads = num_qo_heads
@@ -290,6 +291,7 @@ class BsrAttention:
         cfg.max_partial_rows = max_partial_rows
         cfg.cost_item = cost_item
         cfg.cost_mfma = cost_mfma
+        cfg.slot2_speed = slot2_speed
         self.cfg = cfg
         self.dtype = dtype
         self.device = device
