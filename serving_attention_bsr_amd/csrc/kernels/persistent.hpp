@@ -112,6 +112,8 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   WorkItem nxt;
   if (ib < ie) nxt = load_invariant(items + ib);
   for (int32_t i = ib; i < ie; ++i) {
+    if (i == ib + 1) BSR_STAMP(6);  // (timeline builds: after the first and second items)
+    if (i == ib + 2) BSR_STAMP(7);
     const WorkItem it = nxt;
     if (i + 1 < ie) nxt = load_invariant(items + i + 1);
     if (it.flags & kItemPartial) {
