@@ -74,11 +74,18 @@ __device__ u32x4_t bsr_struct_load_b128(__amdgpu_buffer_rsrc_t rsrc, int vindex,
 // wait for every gather in flight (the next tile's, into the other buffer) before
 // any later LDS read it cannot prove independent, such as the transpose reads.
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void lds_gather_b128(__amdgpu_buffer_rsrc_t rsrc, void* lds, int vindex, int voffset) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+__device__ __forceinline__ void lds_gather_b128(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int vindex,
+                                                int voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
   const i32x2_t va = {vindex, voffset};
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 idxen offen lds" ::"s"(m0), "v"(va), "s"(rsrc)
                : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const void* lds) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+}
+__device__ __forceinline__ void lds_gather_b128(__amdgpu_buffer_rsrc_t rsrc, void* lds, int vindex, int voffset) {
+  lds_gather_b128(rsrc, lds_addr_of(lds), vindex, voffset);
 }
 
 // Element i of a 32-bit array through a raw buffer resource (32-bit offset).

@@ -100,11 +100,11 @@ struct MfmaBody {
     }
   }
 
-  // Gather this lane's rows N0 <= n < N1 of a tile's K and V into a buffer (K at
-  // buf, V at buf + BC * D).  rows_per_page = H_kv * P: pool rows between
-  // consecutive pages.
+  // Gather this lane's rows N0 <= n < N1 of a tile's K and V into the buffer at LDS
+  // byte address buf (K at buf, V at buf + 2 BC D).  rows_per_page = H_kv * P: pool
+  // rows between consecutive pages.
   static __device__ __forceinline__ void gather(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                                uint32_t rows_per_page, const Rows& rows, uint16_t* buf, int wave,
+                                                uint32_t rows_per_page, const Rows& rows, uint32_t buf, int wave,
                                                 int lane, int n0 = 0, int n1 = NI) {
     const int slot = lane % NCH;
 #pragma unroll
@@ -112,9 +112,9 @@ struct MfmaBody {
       if (n < n0 || n >= n1) continue;  // n0, n1 are constants where this is inlined
       const int r = lane_row(wave, lane, n);
       const int row = static_cast<int>(rows.page[n] * rows_per_page + rows.off[n]);
-      uint16_t* dst = buf + (NI * wave + n) * 512;
+      const uint32_t dst = buf + static_cast<uint32_t>(NI * wave + n) * 1024u;
       lds_gather_b128(kr, dst, row, 16 * (slot ^ swz_k(r)));
-      lds_gather_b128(vr, dst + BC * D, row, 16 * (slot ^ swz_v(r)));
+      lds_gather_b128(vr, dst + BC * D * 2, row, 16 * (slot ^ swz_v(r)));
     }
   }
 
@@ -290,11 +290,18 @@ struct MfmaBody {
     // computed and waited for at the next step.
     if (ntiles > 0) {
       load_rows(p, irs, it, 0, wave, lane, rows);
-      gather(krs, vrs, rpp, rows, lds_h, wave, lane);
+      gather(krs, vrs, rpp, rows, lds_addr_of(lds_h), wave, lane);
       if (ntiles > 1) load_rows(p, irs, it, 1, wave, lane, rows);
     }
-    // One tile step: lk is the buffer holding tile t, nb the other one.
-    auto tile = [&](int t, const uint16_t* lk, uint16_t* nb) {
+    // One tile step: buffer cur holds tile t, the other one takes tile t + 1.  The
+    // LDS base is made opaque per step, so the gathers' LDS addresses are formed
+    // next to each load (scalar adds) instead of being computed once for the whole
+    // item and held in scalar registers, which spilled them.
+    auto tile = [&](int t, int cur) {
+      uint32_t lbase = lds_addr_of(lds_h);
+      asm volatile("" : "+s"(lbase));
+      const uint16_t* lk = lds_h + cur * STAGE;
+      const uint32_t nb = lbase + static_cast<uint32_t>((1 - cur) * STAGE * 2);
       // this wavefront's gather of tile t (and the ids of tile t + 1) has landed;
       // after the barrier every wavefront's has, and every wavefront is done with
       // tile t - 1, whose buffer now takes tile t + 1
@@ -317,8 +324,8 @@ struct MfmaBody {
     // tiles in pairs, so that each step's buffers sit at fixed LDS offsets (the
     // reads then take them as immediate offsets instead of per-tile address math)
     for (int t = 0; t < ntiles; t += 2) {
-      tile(t, lds_h, lds_h + STAGE);
-      if (t + 1 < ntiles) tile(t + 1, lds_h + STAGE, lds_h);
+      tile(t, 0);
+      if (t + 1 < ntiles) tile(t + 1, 1);
     }
 
     // result: this lane's column holds O^T[d][rho] for d = 32 db + 8 (r/4) + 4 half + r%4
