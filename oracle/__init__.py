@@ -15,3 +15,4 @@ from .attention import (  # noqa: F401
     merge_states,
 )
 from .append import append_paged_kv, append_slots  # noqa: F401
+from .fp8 import decode_e4m3  # noqa: F401
