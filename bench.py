@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 HEADLINE = "batch_decode"
 ALL = ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill", "shared_prefix_composable",
-       "append_kv_prefill"]
+       "batch_decode_fp8", "append_kv_prefill"]
 # writing the new K/V rows of a workload into its paged cache (not an attention run)
 APPEND = {"append_kv_prefill": "ragged_causal_prefill"}
 
@@ -78,7 +78,10 @@ def roofline(work, ms, traffic, mfma):
 
 def algorithmic_work(w, composable=False):
     """Bytes the method must move and flops it must do (masked pairs excluded)."""
-    elt = 2 if w.dtype == "bf16" else 4
+    elt = 2 if w.dtype == "bf16" else 4            # Q and O
+    kv_elt = 1 if w.dtype == "bf16_kv_fp8" else 2 if w.dtype == "bf16" else 4
+    if w.dtype == "bf16_kv_fp8":
+        elt = 2
     h_qo, h_kv, d = w.num_qo_heads, w.num_kv_heads, w.head_dim
     total_qo = int(w.qo_indptr[-1])
     qol = w.qo_lens.astype(np.int64)
@@ -99,7 +102,7 @@ def algorithmic_work(w, composable=False):
             pair_count = int(np.sum(qol * prefix + qol * (qol + 1) // 2))
         else:
             pair_count = int(np.sum(w.kv_lens * qol))
-    kv_bytes = 2 * keys * h_kv * d * elt
+    kv_bytes = 2 * keys * h_kv * d * kv_elt
     qo_bytes = 2 * total_qo * h_qo * d * elt + total_qo * h_qo * 4
     idx_bytes = 4 * pages
     flops = 4 * d * h_qo * pair_count

@@ -78,7 +78,7 @@ const void* find_kernel(const KernelKey& key, int* wg_per_cu) {
   for (const KernelEntry& e : table) {
     const KernelKey& k = e.key;
     if (k.kind == key.kind && k.bf16 == key.bf16 && k.head_dim == key.head_dim &&
-        k.rows == key.rows && k.cap == key.cap && k.page1 == key.page1) {
+        k.rows == key.rows && k.cap == key.cap && k.page1 == key.page1 && k.kv8 == key.kv8) {
       if (wg_per_cu != nullptr) *wg_per_cu = e.wg_per_cu;
       return e.fn;
     }
@@ -117,8 +117,8 @@ int validate_config(const bsr_attn_config* c) {
     return fail(BSR_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
   if (c->page_size < 1 || c->page_size > (1 << 16))
     return fail(BSR_ERR_INVALID_ARG, "page_size must be in [1, 65536]");
-  if (c->dtype != BSR_DTYPE_F32 && c->dtype != BSR_DTYPE_BF16)
-    return fail(BSR_ERR_INVALID_ARG, "dtype must be BSR_DTYPE_F32 or BSR_DTYPE_BF16");
+  if (c->dtype != BSR_DTYPE_F32 && c->dtype != BSR_DTYPE_BF16 && c->dtype != BSR_DTYPE_BF16_KV_FP8)
+    return fail(BSR_ERR_INVALID_ARG, "dtype must be BSR_DTYPE_F32, BSR_DTYPE_BF16 or BSR_DTYPE_BF16_KV_FP8");
   if (c->causal != 0 && c->causal != 1) return fail(BSR_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (!(c->logits_soft_cap >= 0.0f) || !std::isfinite(c->logits_soft_cap))
     return fail(BSR_ERR_INVALID_ARG, "logits_soft_cap must be finite and >= 0");
@@ -162,7 +162,8 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   bsr_attn* h = new bsr_attn();
   h->cfg = *cfg;
   h->device = device;
-  const bool bf16 = cfg->dtype == BSR_DTYPE_BF16;
+  const bool bf16 = cfg->dtype != BSR_DTYPE_F32;      // Q and O
+  const bool kv8 = cfg->dtype == BSR_DTYPE_BF16_KV_FP8;  // K and V as FP8 codes
   const bool cap = cfg->logits_soft_cap > 0.0f;
   const int g = cfg->num_qo_heads / cfg->num_kv_heads;
 
@@ -189,7 +190,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
     for (int kind = bsr::kKindDecode; kind <= bsr::kKindMixed; ++kind) {
       for (int ri = 0; ri < 2; ++ri) {
         KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : (ri == 0 ? 4 : 8), cap,
-                      kind == bsr::kKindMfma && cfg->page_size == 1};
+                      kind == bsr::kKindMfma && cfg->page_size == 1, kv8};
         int preferred = 1;
         const void* fn = bsr::find_kernel(key, &preferred);
         if (fn == nullptr) continue;  // instance not built for this configuration
@@ -229,6 +230,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.page_size = cfg->page_size;
   pc.causal = cfg->causal != 0;
   pc.bf16 = bf16;
+  pc.kv8 = kv8;
   for (int k = 0; k < 4; ++k) pc.num_wg[k][0] = h->num_wg[k][0], pc.num_wg[k][1] = h->num_wg[k][1];
   pc.alpha = cfg->cost_alpha > 0 ? cfg->cost_alpha : 1;
   pc.beta = cfg->cost_beta > 0 ? cfg->cost_beta : 1;
@@ -312,7 +314,7 @@ static int finish_plan(bsr_attn_t h, std::vector<BlockRow>& rows, int32_t total_
   if (h->device >= 0) {
     fn = bsr::find_kernel(KernelKey{res.kernel, h->pc.bf16, h->pc.head_dim, rows_key,
                                     h->cfg.logits_soft_cap > 0.0f,
-                                    res.kernel == bsr::kKindMfma && h->pc.page_size == 1});
+                                    res.kernel == bsr::kKindMfma && h->pc.page_size == 1, h->pc.kv8});
     if (fn == nullptr)
       return fail(BSR_ERR_UNSUPPORTED, "no kernel built for this plan's kind " + std::to_string(res.kernel));
   }
@@ -512,8 +514,9 @@ int bsr_attn_append_kv(const void* k_new, const void* v_new, const int32_t* appe
     return fail(BSR_ERR_INVALID_ARG, "batch, total_new and num_pages must be >= 0");
   if (num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0)
     return fail(BSR_ERR_INVALID_ARG, "num_kv_heads, head_dim and page_size must be > 0");
-  if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16) return fail(BSR_ERR_INVALID_ARG, "dtype must be F32 or BF16");
-  const int64_t row_bytes = int64_t(head_dim) * (dtype == BSR_DTYPE_F32 ? 4 : 2);
+  if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16 && dtype != BSR_DTYPE_BF16_KV_FP8)
+    return fail(BSR_ERR_INVALID_ARG, "dtype must be F32, BF16 or BF16_KV_FP8");
+  const int64_t row_bytes = int64_t(head_dim) * (dtype == BSR_DTYPE_F32 ? 4 : (dtype == BSR_DTYPE_BF16 ? 2 : 1));
   if (row_bytes % 16 != 0) return fail(BSR_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16 bytes");
   if (total_new == 0 || batch == 0) return BSR_OK;
   if (k_new == nullptr || v_new == nullptr || append_indptr == nullptr || kv_indptr == nullptr ||

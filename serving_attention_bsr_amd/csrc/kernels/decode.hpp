@@ -29,13 +29,22 @@
 
 namespace bsr {
 
-template <int D, bool BF16, int ROWS, int TB, bool CAP>
+// KV8: K and V are OCP FP8 E4M3 codes (one byte per element) while Q and O are
+// bf16; a lane then holds 16 consecutive elements of a KV row in one 16-byte load,
+// and its 16 query elements are the same ones (two 16-byte loads of bf16).  The
+// codes are converted exactly (E4M3 values are bf16 values) by the gfx950
+// conversion instruction, whose decoding of all 256 codes was checked against the
+// format on the GPU.
+template <int D, bool BF16, int ROWS, int TB, bool CAP, bool KV8 = false>
 struct DecodeBody {
+  static_assert(!KV8 || BF16, "an FP8 K/V cache has bf16 queries");
   static constexpr int LPT = D / 16;                 // lanes per KV row
   static constexpr int NG = 64 / LPT;                // KV rows per wavefront step slot
-  static constexpr int ESZ = BF16 ? 2 : 4;           // element bytes
-  static constexpr int NLD = 16 * ESZ / 16;          // 16-byte loads per row per lane
-  static constexpr int EPL = 16 / ESZ;               // elements per 16-byte load
+  static constexpr int QSZ = BF16 ? 2 : 4;           // Q / O element bytes
+  static constexpr int ESZ = KV8 ? 1 : QSZ;          // K / V element bytes
+  static constexpr int NLD = 16 * ESZ / 16;          // 16-byte K/V loads per row per lane
+  static constexpr int EPL = 16 / ESZ;               // elements per 16-byte K/V load
+  static constexpr int QLD = 16 * QSZ / 16;          // 16-byte Q loads per row per lane
   static constexpr int TILE = NG * TB;               // keys per wavefront step
   static constexpr int LDS_FLOATS = kWaves * ROWS * (D + 2);
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
@@ -128,8 +137,25 @@ struct DecodeBody {
     }
   }
 
-  static __device__ __forceinline__ float dot_row(const uint4 (&q)[NLD], const uint4 (&k)[NLD]) {
+  // Two E4M3 codes (the low or high half of w) as a bf16 pair (exact).
+  template <bool HIGH>
+  static __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
+    return pack_bf16x2(f[0], f[1]);
+  }
+
+  static __device__ __forceinline__ float dot_row(const uint4 (&q)[QLD], const uint4 (&k)[NLD]) {
     float s = 0.0f;
+    if constexpr (KV8) {
+      const uint32_t kw[4] = {k[0].x, k[0].y, k[0].z, k[0].w};
+      const uint32_t qw[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        s = dot2_bf16(qw[2 * w], e4m3x2_to_bf16x2<false>(kw[w]), s);
+        s = dot2_bf16(qw[2 * w + 1], e4m3x2_to_bf16x2<true>(kw[w]), s);
+      }
+      return s;
+    }
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       if constexpr (BF16) {
@@ -148,6 +174,19 @@ struct DecodeBody {
   }
 
   static __device__ __forceinline__ void unpack_v(const uint4 (&v)[NLD], float (&out)[16]) {
+    if constexpr (KV8) {
+      const uint32_t vw[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(vw[w]), false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(vw[w]), true);
+        out[4 * w] = lo[0];
+        out[4 * w + 1] = lo[1];
+        out[4 * w + 2] = hi[0];
+        out[4 * w + 3] = hi[1];
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -166,7 +205,7 @@ struct DecodeBody {
   // One tile of keys.  live = false masks every key: the update is then an exact
   // no-op (alpha = 1, p = 0 against finite values).
   static __device__ __forceinline__ void step(const RunParams& p, const WorkItem& it, int tile,
-                                              int grp, bool live, const uint4 (&q)[ROWS][NLD],
+                                              int grp, bool live, const uint4 (&q)[ROWS][QLD],
                                               const Kv& kv, State& st) {
     float s[TB][ROWS];
 #pragma unroll
@@ -232,7 +271,7 @@ struct DecodeBody {
     const int rows_valid = it.qo_count * g;
 
     // folded query rows: row r = token (r / g) of the tile, head kv_head * g + r % g
-    uint4 q[ROWS][NLD];
+    uint4 q[ROWS][QLD];
     {
       const uint8_t* qb = static_cast<const uint8_t*>(p.q);
 #pragma unroll
@@ -240,12 +279,19 @@ struct DecodeBody {
         if (r < rows_valid) {
           const int64_t qrow = static_cast<int64_t>(it.qo_begin + r / g) * p.h_qo +
                                it.kv_head * g + r % g;
-          const uint8_t* src = qb + qrow * (D * ESZ) + c * 16;
+          if constexpr (KV8) {
+            // this lane's 16 consecutive elements c * 16 .. c * 16 + 15
+            const uint8_t* src = qb + qrow * (D * QSZ) + c * 32;
+            q[r][0] = *reinterpret_cast<const uint4*>(src);
+            q[r][1] = *reinterpret_cast<const uint4*>(src + 16);
+          } else {
+            const uint8_t* src = qb + qrow * (D * QSZ) + c * 16;
 #pragma unroll
-          for (int j = 0; j < NLD; ++j) q[r][j] = *reinterpret_cast<const uint4*>(src + j * (LPT * 16));
+            for (int j = 0; j < QLD; ++j) q[r][j] = *reinterpret_cast<const uint4*>(src + j * (LPT * 16));
+          }
         } else {
 #pragma unroll
-          for (int j = 0; j < NLD; ++j) q[r][j] = make_uint4(0, 0, 0, 0);
+          for (int j = 0; j < QLD; ++j) q[r][j] = make_uint4(0, 0, 0, 0);
         }
       }
     }

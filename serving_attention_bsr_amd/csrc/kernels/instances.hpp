@@ -34,6 +34,16 @@ inline void add_decode(std::vector<KernelEntry>* out) {
                   kDecodeWgPerCu});
 }
 
+// FP8 (E4M3) K/V with bf16 Q/O: four KV rows per lane group and step, the bytes in
+// flight of the bf16 body's two.
+template <int D, int ROWS, bool CAP>
+inline void add_decode_kv8(std::vector<KernelEntry>* out) {
+  out->push_back({KernelKey{kKindDecode, true, D, ROWS, CAP, false, true},
+                  reinterpret_cast<const void*>(
+                      &bsr_persistent_kernel<D, true, ROWS, 2 * kDecodeTb<true>, CAP, kKindDecode, 1, false, true>),
+                  kDecodeWgPerCu});
+}
+
 // MFMA kernels: two workgroups per CU, so that one workgroup's softmax and
 // gather run while the other's matrix products do (both MFMA bodies fit 256
 // registers per lane).
@@ -75,6 +85,10 @@ inline void register_head_dim(std::vector<KernelEntry>* out) {
   add_decode<D, false, 4, true>(out);
   add_decode<D, false, 8, false>(out);
   add_decode<D, false, 8, true>(out);
+  add_decode_kv8<D, 4, false>(out);
+  add_decode_kv8<D, 4, true>(out);
+  add_decode_kv8<D, 8, false>(out);
+  add_decode_kv8<D, 8, true>(out);
 }
 
 }  // namespace bsr

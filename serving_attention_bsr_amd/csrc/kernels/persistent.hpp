@@ -37,10 +37,11 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // KIND selects the attention bodies: decode only, MFMA only (bf16), or both
 // (chosen per work item).
-template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, bool PAGE1>
+template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, bool PAGE1, bool KV8>
 struct PersistentKernel {
   static_assert(KIND == kKindDecode || BF16, "the MFMA body is bf16 only");
-  using Decode = DecodeBody<D, BF16, ROWS, TB, CAP>;
+  static_assert(KIND == kKindDecode || !KV8, "an FP8 K/V cache runs on the decode body only");
+  using Decode = DecodeBody<D, BF16, ROWS, TB, CAP, KV8>;
   // 32 rows per wavefront up to D = 128; 16 rows (two workgroups per CU) at D = 256
   using Mfma = typename std::conditional<D == 256, MfmaBody16<D, CAP, PAGE1>, MfmaBody<D, CAP, PAGE1>>::type;
   using Merge = MergeBody<D, BF16>;
@@ -79,10 +80,11 @@ struct PersistentKernel {
 #endif
 
 // OCC: workgroups per CU the register allocation must allow.  PAGE1: the pool has
-// one key per page (MFMA bodies skip the page division).
-template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, int OCC, bool PAGE1 = false>
+// one key per page (MFMA bodies skip the page division).  KV8: K and V are FP8
+// E4M3 codes (decode body; Q and O bf16).
+template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, int OCC, bool PAGE1 = false, bool KV8 = false>
 __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunParams p) {
-  using K = PersistentKernel<D, BF16, ROWS, TB, CAP, KIND, PAGE1>;
+  using K = PersistentKernel<D, BF16, ROWS, TB, CAP, KIND, PAGE1, KV8>;
   __shared__ float lds[K::LDS_FLOATS];
   uint8_t* ws = p.ws;
   // the whole header in one read (its fields are uniform; the empty asm keeps the

@@ -36,6 +36,7 @@ struct KernelKey {
   int rows;  // decode-body folded rows (0 when the kernel has no decode body)
   bool cap;
   bool page1 = false;  // instance specialised for one key per page (MFMA kind only)
+  bool kv8 = false;    // K/V are FP8 E4M3 codes, Q/O bf16 (decode kind only)
 };
 
 // Host stub of the matching persistent kernel, or null if not built; the

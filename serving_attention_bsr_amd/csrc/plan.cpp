@@ -468,10 +468,11 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   int32_t decode_rows = max_decode_rows <= 4 ? 4 : 8;
   int32_t q_tile = decode_rows;
   if (any_wide) {
-    if (!cfg.bf16) {
-      // fp32 has no MFMA body here: long query rows run as tiles of 8 folded rows
+    if (!cfg.bf16 || cfg.kv8) {
+      // fp32 and an FP8 K/V cache have no MFMA body here: long query rows run as
+      // tiles of 8 folded rows
       if (g > kMaxDecodeRows) {
-        *err = "fp32 with more than 8 query heads per KV head is not supported";
+        *err = "fp32 or FP8 K/V with more than 8 query heads per KV head is not supported";
         return BSR_ERR_UNSUPPORTED;
       }
       kernel = kKindDecode;
@@ -513,7 +514,7 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
     const BlockRow& r = rows[ri];
     if (r.qo_len == 0) continue;
     const bool wide = static_cast<int64_t>(r.qo_len) * g > kMaxDecodeRows;
-    const bool mfma = cfg.bf16 && (kernel == kKindMfma || (kernel == kKindMixed && wide));
+    const bool mfma = cfg.bf16 && !cfg.kv8 && (kernel == kKindMfma || (kernel == kKindMixed && wide));
     const int32_t tile_tokens = (mfma ? q_tile : decode_rows) / g;
     for (int32_t h = 0; h < h_kv; ++h) {
       for (int32_t t0 = 0; t0 < r.qo_len; t0 += tile_tokens) {

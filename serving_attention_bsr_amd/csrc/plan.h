@@ -30,6 +30,7 @@ struct PlanConfig {
   // CUs of the device (0 for host-only handles) and the speed of the second
   // workgroup of each CU in a two-per-CU MFMA grid, in sixteenths of the first's
   int32_t cus = 0;
+  bool kv8 = false;  // K/V are FP8 codes: decode body only (no MFMA tiles)
   int32_t slot2_speed16 = 16;
   // capacities (plan rejected beyond them)
   int32_t max_batch = 0, max_total_qo = 0;

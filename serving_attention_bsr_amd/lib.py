@@ -26,6 +26,7 @@ BSR_ERR_HIP = 4
 BSR_ERR_DEVICE = 5
 BSR_DTYPE_F32 = 0
 BSR_DTYPE_BF16 = 1
+BSR_DTYPE_BF16_KV_FP8 = 2
 
 KERNEL_DECODE = 1
 KERNEL_MFMA = 2
@@ -277,7 +278,7 @@ class BsrAttention:
         cfg.num_kv_heads = num_kv_heads
         cfg.head_dim = head_dim
         cfg.page_size = page_size
-        cfg.dtype = BSR_DTYPE_BF16 if dtype == "bf16" else BSR_DTYPE_F32
+        cfg.dtype = {"bf16": BSR_DTYPE_BF16, "f32": BSR_DTYPE_F32, "bf16_kv_fp8": BSR_DTYPE_BF16_KV_FP8}[dtype]
         cfg.causal = int(bool(causal))
         cfg.sm_scale = sm_scale
         cfg.logits_soft_cap = logits_soft_cap
@@ -395,10 +396,12 @@ def append_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, last_page_len,
         raise ValueError("new rows and pools must share one dtype")
     if k_pool.dtype == torch.bfloat16:
         dtype = BSR_DTYPE_BF16
+    elif k_pool.dtype == torch.float8_e4m3fn:
+        dtype = BSR_DTYPE_BF16_KV_FP8
     elif k_pool.dtype == torch.float32:
         dtype = BSR_DTYPE_F32
     else:
-        raise ValueError("dtype must be float32 or bfloat16")
+        raise ValueError("dtype must be float32, bfloat16 or float8_e4m3fn")
     num_pages, h_kv, page_size, d = k_pool.shape
     total_new = k_new.shape[0]
     if tuple(k_new.shape) != (total_new, h_kv, d) or tuple(v_new.shape) != (total_new, h_kv, d):

@@ -29,6 +29,10 @@ import numpy as np
 import torch
 
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+# bf16 queries and outputs over a K/V cache of OCP FP8 E4M3 codes: K and V are
+# drawn like the others and rounded to E4M3 (nearest even) after the unused
+# slots are filled with NaN
+KV_FP8 = "bf16_kv_fp8"
 
 
 @dataclasses.dataclass
@@ -111,6 +115,8 @@ def _draw_tensors(seed, total_q, num_pages, h_qo, h_kv, page_size, d, dtype):
     q = torch.randn((total_q, h_qo, d), generator=gen, dtype=torch.float32)
     k = torch.randn((num_pages, h_kv, page_size, d), generator=gen, dtype=torch.float32)
     v = torch.randn((num_pages, h_kv, page_size, d), generator=gen, dtype=torch.float32)
+    if dtype == KV_FP8:
+        return q.to(torch.bfloat16), k, v  # K, V rounded to E4M3 by the caller, after poisoning
     t = DTYPES[dtype]
     return q.to(t), k.to(t), v.to(t)
 
@@ -179,6 +185,9 @@ def build(
         pages, slots = _used_slots(kv_indptr, kv_indices, last, page_size)
         _poison_unused(k, pages, slots)
         _poison_unused(v, pages, slots)
+    if tensors and dtype == KV_FP8:
+        k = k.to(torch.float8_e4m3fn)
+        v = v.to(torch.float8_e4m3fn)
     return Workload(
         name=name,
         dtype=dtype,
@@ -219,6 +228,13 @@ def batch_decode(seed=2, batch=64, lo=512, hi=8192, tensors=True):
     rng = np.random.Generator(np.random.PCG64(seed))
     kv = rng.integers(lo, hi, size=batch, endpoint=True)
     return build("batch_decode", seed, [1] * batch, kv, 16, 32, 8, 128, dtype="bf16", rng=rng, tensors=tensors)
+
+
+def batch_decode_fp8(seed=6, batch=64, lo=512, hi=8192, tensors=True):
+    """Batch decode with an FP8 (E4M3) K/V cache: the batch decode shapes, bf16 Q/O."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kv = rng.integers(lo, hi, size=batch, endpoint=True)
+    return build("batch_decode_fp8", seed, [1] * batch, kv, 16, 32, 8, 128, dtype=KV_FP8, rng=rng, tensors=tensors)
 
 
 def skewed_long_decode(seed=3, long_len=131072, short_len=1024, n_short=15, cap=30.0, tensors=True):
@@ -319,6 +335,7 @@ def shared_prefix_composable(
 NAMED = {
     "tiny_decode_f32": tiny_decode_f32,
     "batch_decode": batch_decode,
+    "batch_decode_fp8": batch_decode_fp8,
     "skewed_long_decode": skewed_long_decode,
     "ragged_causal_prefill": ragged_causal_prefill,
     "shared_prefix_composable": shared_prefix_composable,

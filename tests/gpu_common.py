@@ -11,7 +11,7 @@ import oracle
 from serving_attention_bsr_amd import lib
 
 # Tolerances: O elementwise |o - ref| <= atol + rtol |ref|, LSE absolute.
-TOL = {"bf16": (1e-2, 1e-2), "f32": (2e-5, 2e-5)}
+TOL = {"bf16": (1e-2, 1e-2), "f32": (2e-5, 2e-5), "bf16_kv_fp8": (1e-2, 1e-2)}
 LSE_TOL = 1e-3
 
 
@@ -64,8 +64,13 @@ def run_gpu(w, h=None, composable=False, **kw):
 
 def oracle_of(w, composable=False):
     q = w.q.double().numpy()
-    k = w.k_pool.float().numpy()
-    v = w.v_pool.float().numpy()
+    if w.k_pool.dtype == torch.float8_e4m3fn:
+        # the oracle decodes the E4M3 codes itself
+        k = oracle.decode_e4m3(w.k_pool.view(torch.uint8).numpy())
+        v = oracle.decode_e4m3(w.v_pool.view(torch.uint8).numpy())
+    else:
+        k = w.k_pool.float().numpy()
+        v = w.v_pool.float().numpy()
     if composable:
         return oracle.composable_attention(
             q, k, v, [f.as_dict() for f in w.formats], w.kv_indices_formats, w.page_size,

@@ -1,0 +1,44 @@
+"""GPU parity of the decode body over an FP8 (OCP E4M3) K/V cache with bf16 Q/O.
+
+The oracle decodes the same E4M3 codes the GPU reads (oracle.decode_e4m3, pinned
+against the format) and runs the plain attention definition; the tolerance is the
+bf16 one.  Cases: head dims 64 / 128 / 256, split chunks with a soft-cap, 8-row
+speculative decode, wide query rows that run as 8-row decode tiles, and the
+batch decode workload with an FP8 cache.
+"""
+
+import pytest
+
+from serving_attention_bsr_amd import workloads as W
+from tests.gpu_common import compare, oracle_of, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, qo_lens, kv_lens, h_qo, h_kv, d, P, causal, cap, nwg
+    ("kv8_d128_p16", [1] * 9, [1, 2, 31, 32, 33, 511, 512, 513, 3000], 32, 8, 128, 16, False, 0.0, 0),
+    ("kv8_d64_split_cap", [1] * 4, [17, 64, 100, 2550], 8, 2, 64, 16, False, 5.0, 16),
+    ("kv8_d256_p7_split", [1] * 3, [10, 300, 900], 16, 4, 256, 7, False, 0.0, 8),
+    ("kv8_rows8_spec_causal", [2, 2, 1], [90, 333, 5], 8, 2, 128, 16, True, 0.0, 0),
+    ("kv8_wide_rows_decode_tiles", [20, 3], [40, 300], 8, 2, 64, 16, True, 0.0, 8),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_kv_fp8_sweep(case):
+    name, qo, kv, h_qo, h_kv, d, P, causal, cap, nwg = case
+    say("case", name)
+    w = W.build(name, 31, qo, kv, P, h_qo, h_kv, d, dtype=W.KV_FP8, causal=causal, cap=cap)
+    o, lse, info = run_gpu(w, num_workgroups=nwg)
+    say("plan", info)
+    ro, rl = oracle_of(w)
+    compare(w, o, lse, ro, rl, name)
+
+
+def test_batch_decode_fp8():
+    say("workload batch_decode_fp8")
+    w = W.named("batch_decode_fp8")
+    o, lse, info = run_gpu(w)
+    say("plan", info)
+    ro, rl = oracle_of(w)
+    compare(w, o, lse, ro, rl, "batch_decode_fp8")
