@@ -138,10 +138,11 @@ struct DecodeBody {
   }
 
   // Two E4M3 codes (the low or high half of w) as a bf16 pair (exact).
+  // (gfx950 scaled conversion with scale 1: exact for all 256 codes, checked on
+  // the GPU against the format)
   template <bool HIGH>
   static __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
-    return pack_bf16x2(f[0], f[1]);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
   }
 
   static __device__ __forceinline__ float dot_row(const uint4 (&q)[QLD], const uint4 (&k)[NLD]) {
@@ -248,14 +249,42 @@ struct DecodeBody {
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.acc[r][e] *= alpha;
     }
+    if constexpr (KV8) {
+      // two keys at a time: acc += p_i v_i + p_j v_j as one bf16 dot product per
+      // element; the codes of the two keys are interleaved byte by byte and
+      // converted to (v_i, v_j) bf16 pairs, the probabilities rounded to bf16
+      // pairs (the running sum keeps them unrounded)
+      static_assert(TB % 2 == 0, "keys in pairs");
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
-      float v[16];
-      unpack_v(kv.v[i], v);
+      for (int i = 0; i < TB; i += 2) {
+        uint32_t pp[ROWS];
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r)
+        for (int r = 0; r < ROWS; ++r) pp[r] = pack_bf16x2(s[i][r], s[i + 1][r]);
+        const uint32_t va[4] = {kv.v[i][0].x, kv.v[i][0].y, kv.v[i][0].z, kv.v[i][0].w};
+        const uint32_t vb[4] = {kv.v[i + 1][0].x, kv.v[i + 1][0].y, kv.v[i + 1][0].z, kv.v[i + 1][0].w};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) st.acc[r][e] = __builtin_fmaf(s[i][r], v[e], st.acc[r][e]);
+        for (int w = 0; w < 4; ++w) {
+          // bytes (a0, b0, a1, b1) and (a2, b2, a3, b3) of elements 4w .. 4w + 3
+          const uint32_t lo = __builtin_amdgcn_perm(vb[w], va[w], 0x05010400u);
+          const uint32_t hi = __builtin_amdgcn_perm(vb[w], va[w], 0x07030602u);
+          const uint32_t pair[4] = {e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo),
+                                    e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi)};
+#pragma unroll
+          for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st.acc[r][4 * w + j] = dot2_bf16(pair[j], pp[r], st.acc[r][4 * w + j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        float v[16];
+        unpack_v(kv.v[i], v);
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) st.acc[r][e] = __builtin_fmaf(s[i][r], v[e], st.acc[r][e]);
+      }
     }
   }
 
