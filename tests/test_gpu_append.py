@@ -95,3 +95,39 @@ def test_append_skips_pages_outside_the_pool():
     gk, gv = _gpu_append(k_pool, v_pool, k_new, v_new, append_indptr, kv_indptr, bad, last)
     assert np.array_equal(_bits(gk), ek[:num_pages])
     assert np.array_equal(_bits(gv), ev[:num_pages])
+
+
+@pytest.mark.gpu
+def test_append_graph_replays():
+    """bsr_attn_append_kv captured in a HIP graph: every replay (with eager work and
+    new rows in between) writes what the eager call writes."""
+    print("case append_graph", flush=True)
+    lens, new, h_kv, d, page_size = [300, 17, 64, 1000], [1, 17, 5, 40], 8, 128, 16
+    k_pool, v_pool, k_new, v_new, append_indptr, kv_indptr, kv_indices, last = _case(lens, new, h_kv, d, page_size,
+                                                                                    "bf16", 12)
+    dev = torch.device("cuda:0")
+    kp, vp = k_pool.to(dev), v_pool.to(dev)
+    kn, vn = k_new.to(dev), v_new.to(dev)
+    idx = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+           for a in (append_indptr, kv_indptr, kv_indices, last)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lib.append_kv(kn, vn, *idx, kp, vp)  # warm the launch path outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lib.append_kv(kn, vn, *idx, kp, vp)
+    for rep in range(3):
+        # fresh rows each time; restore the pools, replay, compare with the oracle
+        kn.copy_(torch.randn(kn.shape, generator=torch.Generator().manual_seed(100 + rep)).to(kn.dtype))
+        vn.copy_(-kn)
+        kp.copy_(k_pool)
+        vp.copy_(v_pool)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ek, ev = oracle.append_paged_kv(_bits(k_pool), _bits(v_pool), _bits(kn.cpu()), _bits(vn.cpu()),
+                                        append_indptr, kv_indptr, kv_indices, last, page_size)
+        assert np.array_equal(_bits(kp.cpu()), ek), f"replay {rep}"
+        assert np.array_equal(_bits(vp.cpu()), ev), f"replay {rep}"

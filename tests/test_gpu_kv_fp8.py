@@ -42,3 +42,26 @@ def test_batch_decode_fp8():
     say("plan", info)
     ro, rl = oracle_of(w)
     compare(w, o, lse, ro, rl, "batch_decode_fp8")
+
+
+def test_kv_fp8_repeat_is_bitwise():
+    """The same plan gives the same bits on repeated runs (FP8 K/V, split chunks)."""
+    import torch
+
+    from tests.gpu_common import handle_for, to_gpu
+
+    say("case kv8_repeat")
+    w = W.build("kv8_repeat", 41, [1] * 6, [5000, 17, 900, 1, 64, 2100], 16, 32, 8, 128, dtype=W.KV_FP8)
+    h = handle_for(w, num_workgroups=64)
+    q, k, v, idx = to_gpu(w)
+    h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    first = None
+    for rep in range(5):
+        o, lse = h.run(q, k, v, idx)
+        torch.cuda.synchronize()
+        h.check()
+        if first is None:
+            first = (o.clone(), lse.clone())
+        else:
+            assert torch.equal(o.view(torch.int16), first[0].view(torch.int16)), rep
+            assert torch.equal(lse.view(torch.int32), first[1].view(torch.int32)), rep
