@@ -214,20 +214,30 @@ struct DecodeBody {
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) s[i][r] = group_sum<LPT>(dot_row(q[r], kv.k[i]));
     const int g = p.group;
+    // logits in base 2 are c * s: without a soft-cap the scale is folded into the
+    // exponent's fma (c > 0, so the maximum of the raw scores gives the maximum);
+    // with one, s is first mapped to cap * tanh(s / cap) in base 2
+    const float c = CAP ? 1.0f : p.scale_log2;
+    if constexpr (CAP) {
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
-      const int tau = it.kv_begin + tile * TILE + i * NG + grp;
-      const bool in_chunk = live && tau < it.kv_end;
+      for (int i = 0; i < TB; ++i)
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float x;
-        if constexpr (CAP) {
-          x = p.cap_log2 * tanh_exp(s[i][r] * p.sm_scale * p.cap_inv);
-        } else {
-          x = s[i][r] * p.scale_log2;
+        for (int r = 0; r < ROWS; ++r) s[i][r] = p.cap_log2 * tanh_exp(s[i][r] * p.sm_scale * p.cap_inv);
+    }
+    // masks only on steps that reach past the chunk end or the causal limit of the
+    // first row (a real branch: most steps lie inside)
+    const int step_base = it.kv_begin + tile * TILE;
+    if (!live || step_base + TILE > it.kv_end || step_base + TILE - 1 > it.causal_limit) {
+      asm volatile("");
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        const int tau = step_base + i * NG + grp;
+        const bool in_chunk = live && tau < it.kv_end;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          const bool visible = in_chunk && tau <= it.causal_limit + r / g;
+          s[i][r] = visible ? s[i][r] : kNegInf;
         }
-        const bool visible = in_chunk && tau <= it.causal_limit + r / g;
-        s[i][r] = visible ? x : kNegInf;
       }
     }
 #pragma unroll
@@ -235,13 +245,13 @@ struct DecodeBody {
       float mx = s[0][r];
 #pragma unroll
       for (int i = 1; i < TB; ++i) mx = __builtin_fmaxf(mx, s[i][r]);
-      const float m_new = __builtin_fmaxf(st.m[r], mx);
+      const float m_new = __builtin_fmaxf(st.m[r], mx * c);
       const float m_use = m_new == kNegInf ? 0.0f : m_new;
       const float alpha = fast_exp2(st.m[r] - m_use);
       float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
-        s[i][r] = fast_exp2(s[i][r] - m_use);
+        s[i][r] = fast_exp2(__builtin_fmaf(s[i][r], c, -m_use));
         psum += s[i][r];
       }
       st.l[r] = st.l[r] * alpha + psum;
