@@ -240,24 +240,34 @@ struct DecodeBody {
         }
       }
     }
+    // lazy reference maximum (see lazy_max): the accumulators are rescaled, in a
+    // real branch, only on steps where some row's reference moved
+    float alpha[ROWS];
+    bool moved = false;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       float mx = s[0][r];
 #pragma unroll
       for (int i = 1; i < TB; ++i) mx = __builtin_fmaxf(mx, s[i][r]);
-      const float m_new = __builtin_fmaxf(st.m[r], mx * c);
+      const float m_new = lazy_max(st.m[r], mx * c);
       const float m_use = m_new == kNegInf ? 0.0f : m_new;
-      const float alpha = fast_exp2(st.m[r] - m_use);
+      alpha[r] = m_new == st.m[r] ? 1.0f : fast_exp2(st.m[r] - m_use);
+      moved |= m_new != st.m[r];
       float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
         s[i][r] = fast_exp2(__builtin_fmaf(s[i][r], c, -m_use));
         psum += s[i][r];
       }
-      st.l[r] = st.l[r] * alpha + psum;
+      st.l[r] = st.l[r] * alpha[r] + psum;
       st.m[r] = m_new;
+    }
+    if (__ballot(moved) != 0) {
+      asm volatile("");
 #pragma unroll
-      for (int e = 0; e < 16; ++e) st.acc[r][e] *= alpha;
+      for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.acc[r][e] *= alpha[r];
     }
     if constexpr (KV8) {
       // two keys at a time: acc += p_i v_i + p_j v_j as one bf16 dot product per
