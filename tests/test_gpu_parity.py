@@ -202,3 +202,30 @@ def test_merge_states_matches_oracle():
     lib.merge_states(oa_t, la_t, t(ob), t(lb), oa_t, la_t)
     torch.cuda.synchronize()
     np.testing.assert_allclose(oa_t.cpu().numpy(), ro, atol=2e-6, rtol=2e-6)
+
+
+def test_two_per_cu_plan_is_balanced_in_time():
+    """On a device handle the two-per-CU MFMA grid gives each CU's second workgroup
+    (ids #CU .. 2 #CU - 1) about 11/16 of the first one's load, and every work item
+    is queued exactly once."""
+    from tests import plan_blob
+
+    w = W.named("ragged_causal_prefill", tensors=False)
+    h = lib.BsrAttention(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, dtype=w.dtype, causal=w.causal,
+                         max_batch=w.batch, max_total_qo=int(w.qo_indptr[-1]), max_total_kv=int(w.kv_lens.sum()),
+                         device=0)
+    info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say("plan", info, "cus", cus)
+    assert info["kernel"] == 2 and info["num_workgroups"] == 2 * cus
+    plan = plan_blob.decode(h.plan_bytes())
+    ptr, items = plan["item_ptr"], plan["items"]
+    assert ptr[-1] == len(items) == info["num_items"]
+    keys = items["kv_end"] - items["kv_begin"]
+    load = np.array([keys[ptr[i]:ptr[i + 1]].sum() for i in range(2 * cus)], dtype=np.float64)
+    ratio = load[cus:].mean() / load[:cus].mean()
+    say("second / first slot load", ratio)
+    assert 0.6 < ratio < 0.78, ratio
+    # every (row block, head, query tile) unit appears once: no duplicated item
+    sig = set(zip(items["qo_begin"].tolist(), items["kv_head"].tolist(), items["kv_begin"].tolist()))
+    assert len(sig) == len(items)
