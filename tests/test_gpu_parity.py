@@ -11,10 +11,6 @@ from tests.gpu_common import compare, handle_for, oracle_of, run_gpu, say, to_gp
 pytestmark = pytest.mark.gpu
 
 
-def _mfma_missing(exc):
-    return isinstance(exc, lib.BsrError) and exc.code == lib.BSR_ERR_UNSUPPORTED
-
-
 SWEEP = [
     # name, qo_lens, kv_lens, h_qo, h_kv, d, P, dtype, causal, cap, nwg
     ("f32_d64_p16", [1, 1, 1, 1], [17, 64, 100, 255], 8, 2, 64, 16, "f32", False, 0.0, 0),
@@ -74,12 +70,7 @@ def test_named_decode(name):
 def test_named_prefill():
     say("workload ragged_causal_prefill")
     w = W.named("ragged_causal_prefill")
-    try:
-        o, lse, info = run_gpu(w)
-    except lib.BsrError as exc:
-        if _mfma_missing(exc):
-            pytest.skip("MFMA tile body not built in this library")
-        raise
+    o, lse, info = run_gpu(w)
     ro, rl = oracle_of(w)
     compare(w, o, lse, ro, rl, "ragged_causal_prefill")
 
@@ -87,12 +78,7 @@ def test_named_prefill():
 def test_named_composable():
     say("workload shared_prefix_composable")
     w = W.named("shared_prefix_composable")
-    try:
-        o, lse, info = run_gpu(w, composable=True)
-    except lib.BsrError as exc:
-        if _mfma_missing(exc):
-            pytest.skip("MFMA tile body not built in this library")
-        raise
+    o, lse, info = run_gpu(w, composable=True)
     ro, rl = oracle_of(w, composable=True)
     compare(w, o, lse, ro, rl, "shared_prefix_composable")
 
