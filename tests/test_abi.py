@@ -3,6 +3,7 @@
 import os
 import re
 
+import numpy as np
 import pytest
 
 from serving_attention_bsr_amd import lib
@@ -66,3 +67,25 @@ def test_create_rejects_bad_cost_mfma():
             lib.BsrAttention(8, 2, 64, 16, num_workgroups=4, device=-1, max_batch=4, max_total_qo=4,
                              max_total_kv=64, cost_mfma=bad)
         assert e.value.code == lib.BSR_ERR_INVALID_ARG
+
+
+def test_create_rejects_bad_slot2_speed():
+    for bad in (-1, 65):
+        with pytest.raises(lib.BsrError) as e:
+            lib.BsrAttention(8, 2, 64, 16, num_workgroups=4, device=-1, max_batch=4, max_total_qo=4,
+                             max_total_kv=64, slot2_speed=bad)
+        assert e.value.code == lib.BSR_ERR_INVALID_ARG
+    for ok in (0, 11, 16):
+        lib.BsrAttention(8, 2, 64, 16, num_workgroups=4, device=-1, max_batch=4, max_total_qo=4, max_total_kv=64,
+                         slot2_speed=ok).close()
+
+
+def test_fp8_kv_handle_plans_decode_only():
+    """An FP8 K/V handle plans every query row on the decode body (8-row tiles for
+    long rows): the plan never uses the MFMA kinds."""
+    h = lib.BsrAttention(8, 2, 64, 16, dtype="bf16_kv_fp8", num_workgroups=8, device=-1, max_batch=4,
+                         max_total_qo=64, max_total_kv=4096, causal=True)
+    info = h.plan(np.array([0, 1, 41], dtype=np.int32), np.array([0, 4, 8], dtype=np.int32),
+                  np.array([16, 16], dtype=np.int32))
+    assert info["kernel"] == 1 and info["q_tile"] == 8
+    h.close()
