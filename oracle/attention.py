@@ -20,6 +20,8 @@ Sources (the FlashInfer explainer page on zenmind.me, "FlashInferÔºöÈù¢Âêë LLM Ê
     query heads share one KV head.
   * Background, challenge 2 (paper section 1): logits soft-cap as a custom score.
   * Section "Reproduction" (paper section 4.2): prefill is run with a causal mask.
+  * Background, "variants" (paper sections 1 and 3.2.3): masks such as a sliding
+    window are one of the variant axes (the LogitsMask functor).
 
 What this oracle computes is the plain definition of attention, with no tiling,
 online softmax, chunking or plan:
@@ -33,6 +35,10 @@ Readings where the pages are silent (each is listed in the design notes):
     the capped logits.
   * Causal masking is aligned bottom-right: query token t (0-based among the l_qo
     new tokens of its request) sees keys j <= l_kv - l_qo + t.
+  * A sliding window of W keys (W >= 1; 0 is no window) uses the same alignment:
+    query token t sees keys j > l_kv - l_qo + t - W, that is the W keys ending at
+    its own position when the mask is also causal.  The window bounds keys from
+    below only; the causal flag bounds them from above.
   * Query head h reads KV head floor(h / g).
   * A request with n pages holds l_kv = (n - 1) * P + last_page_len tokens; a
     request with no pages, and a row whose every key is masked, give O = 0 and
@@ -88,12 +94,14 @@ def gather_request_kv(pool, kv_indptr, kv_indices, last_page_len, r, page_size):
     return np.asarray(pool[pages, :, tau % page_size, :], dtype=np.float64)
 
 
-def attention_dense(q, k, v, scale, cap=0.0, visible=None):
+def attention_dense(q, k, v, scale, cap=0.0, visible=None, lowest=None):
     """Attention state (O, LSE) of query rows q against keys k and values v.
 
     q: [n, D], k and v: [L, D] (float64).  visible: None (every key visible) or an
     int array [n] giving, per query row, the largest visible key index (keys
-    j > visible[i] are masked).  Returns O [n, D] and LSE [n] (natural log).
+    j > visible[i] are masked); lowest: None or an int array [n] giving the
+    smallest visible key index (keys j < lowest[i] are masked).  Returns O [n, D]
+    and LSE [n] (natural log).
 
     The state definition is the one of Terms, "Attention State and ‚äï" (paper
     section 2.2); the cap is the soft-cap of Background, challenge 2.
@@ -113,6 +121,9 @@ def attention_dense(q, k, v, scale, cap=0.0, visible=None):
     if visible is not None:
         cols = np.arange(length)[None, :]
         s = np.where(cols <= np.asarray(visible)[:, None], s, -np.inf)
+    if lowest is not None:
+        cols = np.arange(length)[None, :]
+        s = np.where(cols >= np.asarray(lowest)[:, None], s, -np.inf)
     m = np.max(s, axis=1)
     live = np.isfinite(m)
     if not np.any(live):
@@ -140,6 +151,7 @@ def bsr_attention(
     scale,
     causal=False,
     cap=0.0,
+    window=0,
 ):
     """Attention of ragged queries over a BSR/paged KV cache.
 
@@ -149,7 +161,8 @@ def bsr_attention(
     Ragged packing follows Terms, "ragged tensor"; the page gather follows Core
     mechanism 1; the GQA mapping follows Terms, "GQA head-group fusion"; the causal
     mask is the prefill mask of section "Reproduction" (paper section 4.2), aligned
-    bottom-right as stated in the module notes.
+    bottom-right as stated in the module notes; window > 0 adds the sliding-window
+    mask of the module notes.
     """
     q = np.asarray(q)
     total, h_qo, d = q.shape
@@ -169,6 +182,9 @@ def bsr_attention(
         visible = None
         if causal:
             visible = l_kv - l_qo + np.arange(l_qo)
+        lowest = None
+        if window > 0:
+            lowest = l_kv - l_qo + np.arange(l_qo) - window + 1
         for h in range(h_qo):
             hk = h // g
             o_h, lse_h = attention_dense(
@@ -178,6 +194,7 @@ def bsr_attention(
                 scale,
                 cap,
                 visible,
+                lowest,
             )
             out[q0:q1, h, :] = o_h
             lse[q0:q1, h] = lse_h
