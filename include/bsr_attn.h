@@ -49,8 +49,11 @@
  * Semantics: O = softmax(S) V and LSE = log(sum exp(S)) per query row and head,
  * where S = sm_scale * q.k, then S = cap * tanh(S / cap) when a soft-cap is set,
  * then, for causal handles, key j of a block row is hidden from its t-th query
- * token (0-based) when j > l_kv - l_qo + t.  A row that sees no key gives O = 0
- * and LSE = -inf.
+ * token (0-based) when j > l_kv - l_qo + t, and, with a sliding window of W keys,
+ * when j <= l_kv - l_qo + t - W (a window is one of the mask variants of the
+ * FlashInfer explainer page's Background and paper section 3.2.3; the window ends
+ * at the same bottom-right aligned position as the causal mask).  A row that sees
+ * no key gives O = 0 and LSE = -inf.
  *
  * Ownership: the library allocates no device memory.  The caller allocates the
  * workspace (device) and the staging buffer (host; page-locked for an
@@ -72,7 +75,7 @@
 extern "C" {
 #endif
 
-#define BSR_ATTN_ABI_VERSION 1
+#define BSR_ATTN_ABI_VERSION 2
 
 typedef enum bsr_status {
   BSR_OK = 0,
@@ -118,6 +121,11 @@ typedef struct bsr_attn_config {
                               in sixteenths; the planner balances their loads in time
                               (Core mechanism 6 balances in cost).  0 selects the
                               measured default, 16 treats them as equal */
+  int32_t sliding_window;  /* 0: no window.  W >= 1: each query sees only keys inside
+                              the window of W keys described above; bsr_attn_plan only
+                              (bsr_attn_plan_composable rejects it).  The planner gives
+                              each query tile only the keys its window can reach */
+  int32_t reserved;        /* must be 0 */
 } bsr_attn_config;
 
 /* One BSR sub-matrix for bsr_attn_plan_composable().  Arrays are host memory. */

@@ -131,6 +131,8 @@ int validate_config(const bsr_attn_config* c) {
     return fail(BSR_ERR_INVALID_ARG, "negative tuning parameter");
   if (c->cost_mfma > 16 * 256) return fail(BSR_ERR_INVALID_ARG, "cost_mfma too large");
   if (c->slot2_speed > 64) return fail(BSR_ERR_INVALID_ARG, "slot2_speed too large");
+  if (c->sliding_window < 0) return fail(BSR_ERR_INVALID_ARG, "sliding_window must be >= 0");
+  if (c->reserved != 0) return fail(BSR_ERR_INVALID_ARG, "reserved must be 0");
   return BSR_OK;
 }
 
@@ -242,6 +244,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.mfma_w16 = cfg->cost_mfma > 0 ? cfg->cost_mfma : 192;
   pc.cus = h->cus;
   pc.slot2_speed16 = cfg->slot2_speed > 0 ? cfg->slot2_speed : kSlot2Speed16;
+  pc.window = cfg->sliding_window;
   pc.max_batch = cfg->max_batch;
   pc.max_total_qo = cfg->max_total_qo;
   pc.max_total_kv = cfg->max_total_kv;
@@ -386,6 +389,8 @@ int bsr_attn_plan_composable(bsr_attn_t h, int32_t num_formats, const bsr_format
                              int32_t total_qo, void* workspace, void* host_staging, void* stream) {
   if (h == nullptr) return fail(BSR_ERR_INVALID_ARG, "handle is null");
   if (h->cfg.causal) return fail(BSR_ERR_UNSUPPORTED, "composed formats are not supported with causal masking");
+  if (h->cfg.sliding_window > 0)
+    return fail(BSR_ERR_UNSUPPORTED, "composed formats are not supported with a sliding window");
   if (num_formats < 1 || formats == nullptr) return fail(BSR_ERR_INVALID_ARG, "need at least one format");
   if (total_qo < 0 || total_qo > h->cfg.max_total_qo)
     return fail(total_qo < 0 ? BSR_ERR_INVALID_ARG : BSR_ERR_CAPACITY, "total_qo outside [0, max_total_qo]");

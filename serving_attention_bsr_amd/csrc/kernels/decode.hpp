@@ -225,9 +225,11 @@ struct DecodeBody {
         for (int r = 0; r < ROWS; ++r) s[i][r] = p.cap_log2 * tanh_exp(s[i][r] * p.sm_scale * p.cap_inv);
     }
     // masks only on steps that reach past the chunk end or the causal limit of the
-    // first row (a real branch: most steps lie inside)
+    // first row, or below the sliding-window start of the last token (a real
+    // branch: most steps lie inside)
     const int step_base = it.kv_begin + tile * TILE;
-    if (!live || step_base + TILE > it.kv_end || step_base + TILE - 1 > it.causal_limit) {
+    if (!live || step_base + TILE > it.kv_end || step_base + TILE - 1 > it.causal_limit ||
+        step_base < it.window_lo + it.qo_count) {
       asm volatile("");
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
@@ -235,7 +237,7 @@ struct DecodeBody {
         const bool in_chunk = live && tau < it.kv_end;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-          const bool visible = in_chunk && tau <= it.causal_limit + r / g;
+          const bool visible = in_chunk && tau <= it.causal_limit + r / g && tau >= it.window_lo + r / g;
           s[i][r] = visible ? s[i][r] : kNegInf;
         }
       }

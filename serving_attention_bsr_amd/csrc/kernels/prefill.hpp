@@ -157,16 +157,18 @@ struct MfmaBody {
         for (int r = 0; r < 16; ++r) s[kb][r] = p.cap_log2 * tanh_exp(s[kb][r] * p.sm_scale * p.cap_inv);
     }
     const int tile_base = it.kv_begin + t * BC;
-    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit) {
+    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit || tile_base < it.window_lo + it.qo_count) {
       // key 32 kb + 8 (r / 4) + 4 half + r % 4 of the tile is visible up to the
       // chunk end and this row's causal limit
       asm volatile("");  // keep this a branch: only boundary tiles pay for the mask
       const int lim = min(it.kv_end - 1, it.causal_limit + t_local) - tile_base - 4 * half;
+      // and from this row's sliding-window start on
+      const int low = max(it.window_lo + t_local, it.kv_begin) - tile_base - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = kNegInf;
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim || 32 * kb + 8 * (r >> 2) + (r & 3) < low) s[kb][r] = kNegInf;
     }
   }
 

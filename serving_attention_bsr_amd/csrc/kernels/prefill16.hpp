@@ -140,16 +140,18 @@ struct MfmaBody16 {
         for (int i = 0; i < 4; ++i) s[kb][i] = p.cap_log2 * tanh_exp(s[kb][i] * p.sm_scale * p.cap_inv);
     }
     const int tile_base = it.kv_begin + t * BC;
-    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit) {
+    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit || tile_base < it.window_lo + it.qo_count) {
       asm volatile("");  // keep this a branch: only boundary tiles pay for the mask
       // key 16 kb + 4 grp + i of the tile is visible up to the chunk end and this
       // row's causal limit
       const int lim = min(it.kv_end - 1, it.causal_limit + t_local) - tile_base - 4 * grp;
+      // and from this row's sliding-window start on
+      const int low = max(it.window_lo + t_local, it.kv_begin) - tile_base - 4 * grp;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (16 * kb + i > lim) s[kb][i] = kNegInf;
+          if (16 * kb + i > lim || 16 * kb + i < low) s[kb][i] = kNegInf;
     }
   }
 

@@ -34,6 +34,7 @@ constexpr int32_t kPlanMagic = 0x41525342;  // "BSRA"
 constexpr int kWgThreads = 256;             // 4 wavefronts of 64
 constexpr int kWaves = 4;
 constexpr int32_t kNoCausal = 0x3fffffff;   // causal_limit meaning "every key visible"
+constexpr int32_t kNoWindow = -0x3fffffff;  // window_lo meaning "no lower bound"
 
 enum KernelKind : int32_t { kKindDecode = 1, kKindMfma = 2, kKindMixed = 3 };
 
@@ -57,7 +58,7 @@ struct WorkItem {  // 48 bytes
   int32_t causal_limit;  // token i of the tile sees keys j <= causal_limit + i
   int32_t partial_row;   // first folded row of the partial state, or -1
   int32_t flag_id;       // ready-flag slot of the partial state, or -1
-  int32_t pad0;
+  int32_t window_lo;     // token i of the tile sees keys j >= window_lo + i
   int32_t pad1;
 };
 

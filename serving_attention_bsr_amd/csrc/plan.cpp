@@ -53,8 +53,10 @@ struct Unit {
   int32_t row;
   int32_t head;
   int32_t t0, nt;
-  int32_t l_eff;
+  int32_t kv_lo;  // first key the unit reads (0 unless a sliding window cuts keys off)
+  int32_t l_eff;  // keys the unit reads: kv_lo .. kv_lo + l_eff - 1
   int32_t causal_limit;
+  int32_t window_lo;
   bool mfma;
   int32_t w16;  // cost of one KV token in sixteenths (16 except MFMA units of a mixed grid)
 };
@@ -163,6 +165,7 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
     w.kv_head = u.head;
     w.page_begin = r.page_begin;
     w.causal_limit = u.causal_limit;
+    w.window_lo = u.window_lo;
     w.partial_row = -1;
     w.flag_id = -1;
     return w;
@@ -188,8 +191,8 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
       const int64_t n = ceil_div(u.l_eff, unit_chunk(u, chunk));
       const int64_t csz = n == 1 ? u.l_eff : round_up(ceil_div(u.l_eff, n), kChunkGranule);
       for (int64_t b = 0; b < u.l_eff; b += csz) {
-        w.kv_begin = static_cast<int32_t>(b);
-        w.kv_end = static_cast<int32_t>(std::min<int64_t>(b + csz, u.l_eff));
+        w.kv_begin = static_cast<int32_t>(u.kv_lo + b);
+        w.kv_end = static_cast<int32_t>(u.kv_lo + std::min<int64_t>(b + csz, u.l_eff));
         items.push_back({w, item_cost(ui, w.kv_end - w.kv_begin), ui, 0});
       }
     }
@@ -220,8 +223,8 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
       Slot s = heap.top();
       heap.pop();
       WorkItem w = template_of(ui);
-      w.kv_begin = static_cast<int32_t>(b);
-      w.kv_end = static_cast<int32_t>(e);
+      w.kv_begin = static_cast<int32_t>(units[ui].kv_lo + b);
+      w.kv_end = static_cast<int32_t>(units[ui].kv_lo + e);
       const int64_t c = item_cost(ui, e - b);
       order.push_back(static_cast<int32_t>(items.size()));
       owner.push_back(s.second);
@@ -527,13 +530,24 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
         // the two bodies differ in time per KV token; only a grid that runs both
         // needs the weight (single-body plans keep the pages' key counts)
         u.w16 = kernel == kKindMixed && mfma ? std::max(cfg.mfma_w16, 1) : 16;
+        int32_t end;
         if (cfg.causal) {
           u.causal_limit = r.kv_len - r.qo_len + t0;
-          u.l_eff = std::min<int32_t>(r.kv_len, u.causal_limit + u.nt);
+          end = std::min<int32_t>(r.kv_len, u.causal_limit + u.nt);
         } else {
           u.causal_limit = kNoCausal;
-          u.l_eff = r.kv_len;
+          end = r.kv_len;
         }
+        // a sliding window hides keys below window_lo + t from token t: the unit
+        // starts at its first token's window, rounded down to the chunk granule so
+        // chunk starts stay where the bodies expect them
+        u.window_lo = kNoWindow;
+        u.kv_lo = 0;
+        if (cfg.window > 0) {
+          u.window_lo = r.kv_len - r.qo_len + t0 - cfg.window + 1;
+          u.kv_lo = std::min(std::max(u.window_lo, 0), std::max(end - 1, 0)) / kChunkGranule * kChunkGranule;
+        }
+        u.l_eff = std::max(end - u.kv_lo, 0);
         units.push_back(u);
       }
     }

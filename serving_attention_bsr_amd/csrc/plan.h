@@ -32,6 +32,7 @@ struct PlanConfig {
   int32_t cus = 0;
   bool kv8 = false;  // K/V are FP8 codes: decode body only (no MFMA tiles)
   int32_t slot2_speed16 = 16;
+  int32_t window = 0;  // sliding window in keys (0: none)
   // capacities (plan rejected beyond them)
   int32_t max_batch = 0, max_total_qo = 0;
   int64_t max_total_kv = 0;

@@ -75,6 +75,8 @@ class bsr_attn_config(ctypes.Structure):
         ("cost_item", ctypes.c_int32),
         ("cost_mfma", ctypes.c_int32),
         ("slot2_speed", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -110,6 +112,7 @@ class bsr_plan_info(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 2  # BSR_ATTN_ABI_VERSION of the struct layouts above
 
 
 def load():
@@ -140,6 +143,9 @@ def load():
     for name in EXPORTED:
         if name not in ("bsr_attn_last_error", "bsr_attn_destroy"):
             getattr(lib, name).restype = c_int
+    if lib.bsr_attn_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.bsr_attn_abi_version()}, this binding expects "
+                          f"{ABI_VERSION}; rebuild it with __graft_entry__.build()")
     _lib = lib
     return lib
 
@@ -272,6 +278,7 @@ class BsrAttention:
         cost_item: int = 0,
         cost_mfma: int = 0,
         slot2_speed: int = 0,
+        sliding_window: int = 0,
     ):
         cfg = bsr_attn_config()
         cfg.num_qo_heads = num_qo_heads
@@ -293,6 +300,7 @@ class BsrAttention:
         cfg.cost_item = cost_item
         cfg.cost_mfma = cost_mfma
         cfg.slot2_speed = slot2_speed
+        cfg.sliding_window = sliding_window
         self.cfg = cfg
         self.dtype = dtype
         self.device = device

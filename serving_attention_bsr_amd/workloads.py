@@ -73,6 +73,8 @@ class Workload:
     v_pool: torch.Tensor
     # composed (multi-format) description of the same KV matrix, if any
     formats: Optional[List[Format]] = None
+    # sliding window in keys (0: none)
+    window: int = 0
     kv_indices_formats: Optional[np.ndarray] = None
 
     @property
@@ -160,6 +162,7 @@ def build(
     rng: Optional[np.random.Generator] = None,
     poison: bool = True,
     tensors: bool = True,
+    window: int = 0,
 ) -> Workload:
     """A single-format workload from explicit lengths (lengths drawn by the caller).
 
@@ -205,6 +208,7 @@ def build(
         q=q,
         k_pool=k,
         v_pool=v,
+        window=window,
     )
 
 

@@ -28,6 +28,7 @@ def handle_for(w, **kw):
         dtype=w.dtype,
         causal=w.causal,
         logits_soft_cap=w.cap,
+        sliding_window=w.window,
         max_batch=max(w.batch, 1) + (len(w.formats[1].qo_indptr) if w.formats else 0),
         max_total_qo=max(int(w.qo_indptr[-1]), 1),
         max_total_kv=max(int(w.kv_lens.sum()), 1),
@@ -78,7 +79,7 @@ def oracle_of(w, composable=False):
         )
     return oracle.bsr_attention(
         q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, w.page_size,
-        w.num_qo_heads, w.num_kv_heads, w.scale, w.causal, w.cap,
+        w.num_qo_heads, w.num_kv_heads, w.scale, w.causal, w.cap, w.window,
     )
 
 

@@ -24,7 +24,7 @@ HEADER_FIELDS = [
 ITEM = np.dtype([
     ("flags", "<i4"), ("qo_begin", "<i4"), ("qo_count", "<i4"), ("kv_head", "<i4"),
     ("page_begin", "<i4"), ("kv_begin", "<i4"), ("kv_end", "<i4"), ("causal_limit", "<i4"),
-    ("partial_row", "<i4"), ("flag_id", "<i4"), ("pad0", "<i4"), ("pad1", "<i4"),
+    ("partial_row", "<i4"), ("flag_id", "<i4"), ("window_lo", "<i4"), ("pad1", "<i4"),
 ])
 TASK = np.dtype([("qo_row", "<i4"), ("kv_head", "<i4"), ("src_begin", "<i4"), ("src_count", "<i4")])
 SRC = np.dtype([("partial_row", "<i4"), ("flag_id", "<i4")])
@@ -72,7 +72,7 @@ def execute(plan, q, k_pool, v_pool, kv_indices, group, page_size, scale, cap):
             for t in range(int(it["qo_count"])):
                 token = int(it["qo_begin"]) + t
                 limit = int(it["causal_limit"]) + t
-                vis = tau <= limit
+                vis = (tau <= limit) & (tau >= int(it["window_lo"]) + t)
                 for j in range(group):
                     head = int(it["kv_head"]) * group + j
                     o1, l1 = oracle.attention_dense(

@@ -28,12 +28,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert lib.bsr_attn_abi_version() == 1
+    assert lib.bsr_attn_abi_version() == 2
 
 
 def test_struct_sizes_match_header():
-    # bsr_attn_config: 8 int32/float, max_batch, max_total_qo, int64, 7 int32, reserved[1]
-    assert lib.ctypes.sizeof(lib.bsr_attn_config) == 80
+    # bsr_attn_config: 8 int32/float, max_batch, max_total_qo, int64, 9 int32, reserved
+    assert lib.ctypes.sizeof(lib.bsr_attn_config) == 88
     assert lib.ctypes.sizeof(lib.bsr_plan_info) == 64
 
 

@@ -270,3 +270,67 @@ def test_empty_batch_plans():
     h = host_handle(8, 2, 64, 16)
     info = h.plan([0], [0], [])
     assert info["num_items"] == 0 and info["num_merge_tasks"] == 0
+
+
+WINDOW_CASES = [
+    # name, qo_lens, kv_lens, h_qo, h_kv, d, P, dtype, causal, nwg, window
+    ("decode_window_split", [1, 1, 1, 1], [17, 640, 1000, 2550], 8, 2, 64, 16, "f32", False, 16, 300),
+    ("prefill_causal_window", [40, 7, 300], [100, 7, 900], 8, 2, 64, 1, "bf16", True, 8, 129),
+    ("noncausal_window", [33, 1], [90, 450], 4, 1, 64, 2, "bf16", False, 5, 64),
+    ("window_one", [5, 1, 2], [5, 70, 200], 4, 2, 64, 3, "bf16", True, 4, 1),
+    ("window_covers_all", [3, 1], [50, 90], 4, 2, 64, 16, "bf16", True, 4, 1000),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_window_plan_executes_to_oracle(case):
+    """A sliding-window plan reproduces the oracle's windowed attention, and its
+    items read no key below the first token's window (rounded down to the 64-key
+    chunk granule)."""
+    name, qo, kv, h_qo, h_kv, d, P, dtype, causal, nwg, window = case
+    w = W.build(name, 8, qo, kv, P, h_qo, h_kv, d, dtype=dtype, causal=causal, window=window)
+    h = host_handle(h_qo, h_kv, d, P, dtype, causal, 0.0, nwg, sliding_window=window)
+    h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    plan = plan_blob.decode(h.plan_bytes())
+    q, k, v = f64(w.q), f64(w.k_pool), f64(w.v_pool)
+    o, lse, written = plan_blob.execute(plan, q, k, v, w.kv_indices, w.group, P, w.scale, 0.0)
+    ro, rl = oracle.bsr_attention(q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, P, h_qo, h_kv,
+                                  w.scale, causal, 0.0, window)
+    assert np.all(written == 1)
+    np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-12)
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], rl[fin], rtol=1e-12, atol=1e-12)
+    qo_ptr = np.asarray(w.qo_indptr)
+    for it in plan["items"]:
+        r = int(np.searchsorted(qo_ptr, int(it["qo_begin"]), side="right")) - 1
+        t0 = int(it["qo_begin"]) - int(qo_ptr[r])
+        first = kv[r] - qo[r] + t0 - window + 1
+        assert int(it["window_lo"]) == first
+        assert int(it["kv_begin"]) >= max(first, 0) // 64 * 64, name
+
+
+def test_window_shortens_long_decode_plans():
+    """Decode over 4096 keys with a 256-key window plans about 256 keys per request."""
+    qo, kv = [1] * 4, [4096] * 4
+    w = W.build("window_decode", 9, qo, kv, 16, 8, 2, 64, tensors=False)
+    h = host_handle(8, 2, 64, 16, "bf16", True, 0.0, 8, sliding_window=256)
+    h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    plan = plan_blob.decode(h.plan_bytes())
+    keys = sum(int(it["kv_end"]) - int(it["kv_begin"]) for it in plan["items"])
+    assert keys <= 4 * 2 * (256 + 64), keys
+
+
+def test_composable_plan_rejects_window():
+    h = host_handle(8, 2, 64, 16, sliding_window=16)
+    fmt = dict(qo_indptr=np.array([0, 1], dtype=np.int32), kv_indptr=np.array([0, 1], dtype=np.int32),
+               last_page_len=np.array([4], dtype=np.int32), kv_indices_offset=0)
+    with pytest.raises(lib.BsrError) as e:
+        h.plan_composable([fmt], 1)
+    assert e.value.code == lib.BSR_ERR_UNSUPPORTED
+
+
+def test_create_rejects_negative_window():
+    with pytest.raises(lib.BsrError) as e:
+        host_handle(8, 2, 64, 16, sliding_window=-1)
+    assert e.value.code == lib.BSR_ERR_INVALID_ARG
