@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 HEADLINE = "batch_decode"
 ALL = ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill", "shared_prefix_composable",
-       "batch_decode_fp8", "append_kv_prefill"]
+       "batch_decode_fp8", "batch_decode_window", "append_kv_prefill"]
 # writing the new K/V rows of a workload into its paged cache (not an attention run)
 APPEND = {"append_kv_prefill": "ragged_causal_prefill"}
 
@@ -94,6 +94,18 @@ def algorithmic_work(w, composable=False):
             keys += int(lens.sum())
             pages += int(n.sum())
         pair_count = int(np.sum(w.kv_lens * qol))  # every branch attends prefix + suffix
+    elif w.window > 0:
+        # a sliding window: the keys of a request are those its first token's window
+        # reaches and beyond, its pairs the keys each token sees
+        keys = pages = pair_count = 0
+        for lq, lk in zip(qol, w.kv_lens.astype(np.int64)):
+            pos = lk - lq + np.arange(lq)
+            lo = np.maximum(pos - w.window + 1, 0)
+            hi = pos + 1 if w.causal else np.full(lq, lk)
+            if lq:
+                keys += int(lk - lo[0])
+                pages += int((lk + w.page_size - 1) // w.page_size - lo[0] // w.page_size)
+                pair_count += int(np.sum(hi - lo))
     else:
         keys = int(w.kv_lens.sum())
         pages = int(np.diff(w.kv_indptr.astype(np.int64)).sum())
@@ -157,7 +169,7 @@ def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
     h = lib.BsrAttention(
         w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, dtype=w.dtype, causal=w.causal,
         logits_soft_cap=w.cap, max_batch=max_batch, max_total_qo=int(w.qo_indptr[-1]),
-        max_total_kv=int(w.kv_lens.sum()), device=0, num_workgroups=nwg,
+        max_total_kv=int(w.kv_lens.sum()), device=0, num_workgroups=nwg, sliding_window=w.window,
     )
     work = algorithmic_work(w, composable)
     out = dict(workload=name, dtype=w.dtype, bytes=work["bytes"], flops=work["flops"])
@@ -272,7 +284,7 @@ def cpu_baseline(w, budget_s=10.0):
         while True:
             oracle.bsr_attention(
                 q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, w.page_size,
-                w.num_qo_heads, w.num_kv_heads, w.scale, w.causal, w.cap,
+                w.num_qo_heads, w.num_kv_heads, w.scale, w.causal, w.cap, w.window,
             )
             reps += 1
             if time.perf_counter() - t0 >= budget_s:

@@ -234,6 +234,15 @@ def batch_decode(seed=2, batch=64, lo=512, hi=8192, tensors=True):
     return build("batch_decode", seed, [1] * batch, kv, 16, 32, 8, 128, dtype="bf16", rng=rng, tensors=tensors)
 
 
+def batch_decode_window(seed=7, batch=64, lo=512, hi=8192, window=4096, tensors=True):
+    """Batch decode with a 4096-key sliding window: the batch decode shapes, bf16;
+    requests longer than the window read only its last 4096 keys."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kv = rng.integers(lo, hi, size=batch, endpoint=True)
+    return build("batch_decode_window", seed, [1] * batch, kv, 16, 32, 8, 128, dtype="bf16", rng=rng,
+                 tensors=tensors, window=window)
+
+
 def batch_decode_fp8(seed=6, batch=64, lo=512, hi=8192, tensors=True):
     """Batch decode with an FP8 (E4M3) K/V cache: the batch decode shapes, bf16 Q/O."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -340,6 +349,7 @@ NAMED = {
     "tiny_decode_f32": tiny_decode_f32,
     "batch_decode": batch_decode,
     "batch_decode_fp8": batch_decode_fp8,
+    "batch_decode_window": batch_decode_window,
     "skewed_long_decode": skewed_long_decode,
     "ragged_causal_prefill": ragged_causal_prefill,
     "shared_prefix_composable": shared_prefix_composable,

@@ -57,7 +57,7 @@ def test_sweep(case):
     compare(w, o, lse, ro, rl, name)
 
 
-@pytest.mark.parametrize("name", ["tiny_decode_f32", "batch_decode", "skewed_long_decode"])
+@pytest.mark.parametrize("name", ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "batch_decode_window"])
 def test_named_decode(name):
     say("workload", name)
     w = W.named(name)
