@@ -24,7 +24,8 @@
 //   6. partial states get fixed slots; every query token whose result is split
 //      gets a merge task listing its partial states in KV order (format order
 //      first for composed formats), and merge tasks are spread the same way.
-// Steps 4-6 are evaluated for L_kv and for L_kv / k (k <= kChunkCandidates); the
+// Steps 4-6 are evaluated for L_kv, for L_kv / k (k <= kChunkCandidates) and as fills
+// at L_kv and L_kv / 2; the
 // plan with the smallest predicted makespan is kept, the pages' L_kv unless a
 // finer cut is better by more than 3 % (finer cuts help when indivisible short
 // units leave some workgroups over-full).  Ties are broken by creation order, so
@@ -566,11 +567,18 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   Schedule best;
   bool have = false;
   int64_t last_chunk = -1;
-  for (int k = 1; k <= kChunkCandidates + 1; ++k) {
-    // candidates: the pages' L_kv, L_kv / k (k = 2..), then filling at L_kv
-    const bool fill = k == kChunkCandidates + 1;
+  for (int k = 1; k <= kChunkCandidates + 2; ++k) {
+    // candidates: the pages' L_kv, L_kv / k (k = 2..), then filling at L_kv and at
+    // L_kv / 2 (the latter cuts units of more than half of L_kv only where a
+    // workgroup's room ends: when more units than workgroups are a little over
+    // L_kv / 2 long, as under a sliding window, whole units cannot balance and
+    // halving every one costs an item and a merge each)
+    const bool fill = k > kChunkCandidates;
+    const int64_t fill_chunk = k == kChunkCandidates + 1
+                                   ? base_chunk
+                                   : std::max<int64_t>(round_up(ceil_div(base_chunk, 2), kChunkGranule), min_chunk);
     int64_t chunk =
-        fill ? base_chunk : std::max<int64_t>(round_up(ceil_div(base_chunk, k), kChunkGranule), min_chunk);
+        fill ? fill_chunk : std::max<int64_t>(round_up(ceil_div(base_chunk, k), kChunkGranule), min_chunk);
     // chunks at least as long as every unit cut nothing: all such candidates, and
     // filling without long units, are the same plan
     if (chunk >= max_leff) {

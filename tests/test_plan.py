@@ -334,3 +334,14 @@ def test_create_rejects_negative_window():
     with pytest.raises(lib.BsrError) as e:
         host_handle(8, 2, 64, 16, sliding_window=-1)
     assert e.value.code == lib.BSR_ERR_INVALID_ARG
+
+
+def test_window_batch_is_balanced_by_the_half_chunk_fill():
+    """Under a 4096-key window most decode units are a little over L_kv / 2 long;
+    whole units would leave workgroups with two of them (max/mean 1.17).  The plan
+    cuts some of them and stays within 10 % of the mean."""
+    w = W.named("batch_decode_window", tensors=False)
+    h = host_handle(32, 8, 128, 16, "bf16", False, 0.0, 256, max_batch=64, sliding_window=w.window)
+    info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    assert info["num_partial_items"] > 0
+    assert info["max_wg_cost"] <= 1.10 * info["total_cost"] / 256
