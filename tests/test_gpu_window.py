@@ -1,4 +1,5 @@
-"""GPU parity of the sliding-window mask against the oracle.
+"""GPU parity of the sliding-window mask against the oracle, with bitwise repeat
+and graph replay after a re-plan.
 
 The window is one of the mask variants of the FlashInfer explainer page
 (Background, and paper section 3.2.3's LogitsMask functor); a query token sees
@@ -40,3 +41,79 @@ def test_window_matches_oracle(case):
     say("plan", info)
     ro, rl = oracle_of(w)
     compare(w, o, lse, ro, rl, name)
+
+
+@pytest.mark.gpu
+def test_window_repeat_runs_are_bitwise_identical():
+    """A windowed plan with split chunks and merges gives the same bits on every run."""
+    import torch
+
+    from tests.gpu_common import handle_for, to_gpu
+
+    say("case window_repeat")
+    w = W.named("batch_decode_window", batch=16, lo=100, hi=6000, window=1000)
+    h = handle_for(w)
+    q, k, v, idx = to_gpu(w)
+    info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    assert info["num_partial_items"] > 0, "the case must exercise the merge"
+    o0, l0 = h.run(q, k, v, idx)
+    o0, l0 = o0.clone(), l0.clone()
+    for _ in range(5):
+        o, l = h.run(q, k, v, idx)
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16))
+        assert torch.equal(l.view(torch.int32), l0.view(torch.int32))
+    h.check()
+    ro, rl = oracle_of(w)
+    compare(w, o0.double().cpu().numpy(), l0.double().cpu().numpy(), ro, rl, "window_repeat")
+
+
+@pytest.mark.gpu
+def test_window_graph_replays_after_replan():
+    """A captured windowed run() replays the current plan: re-plan new lengths and
+    replay again; every replay matches the oracle."""
+    import numpy as np
+    import torch
+
+    from tests.gpu_common import handle_for
+
+    say("case window_graph")
+    w1 = W.named("batch_decode_window", seed=41, batch=24, lo=64, hi=4000, window=700)
+    w2 = W.named("batch_decode_window", seed=42, batch=24, lo=64, hi=4000, window=700)
+    dev = torch.device("cuda:0")
+    n_pages = max(w1.k_pool.shape[0], w2.k_pool.shape[0])
+    n_idx = max(len(w1.kv_indices), len(w2.kv_indices))
+    q = torch.empty(w1.q.shape, dtype=w1.q.dtype, device=dev)
+    k = torch.empty((n_pages,) + tuple(w1.k_pool.shape[1:]), dtype=w1.k_pool.dtype, device=dev)
+    v = torch.empty_like(k)
+    idx = torch.zeros(n_idx, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    h = handle_for(w1, max_total_kv=int(max(w1.kv_lens.sum(), w2.kv_lens.sum())))
+
+    def load(w):
+        q.copy_(w.q)
+        k[: w.k_pool.shape[0]].copy_(w.k_pool)
+        v[: w.v_pool.shape[0]].copy_(w.v_pool)
+        idx[: len(w.kv_indices)].copy_(torch.from_numpy(np.ascontiguousarray(w.kv_indices)))
+        h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+        torch.cuda.synchronize()
+
+    load(w1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        h.run(q, k, v, idx, o, lse)  # warm the launch path outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        h.run(q, k, v, idx, o, lse)
+    for w, label in ((w1, "first plan"), (w2, "re-plan")):
+        if w is w2:
+            load(w2)
+        ro, rl = oracle_of(w)
+        for rep in range(2):
+            o.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            compare(w, o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, f"{label} replay {rep}")
+    h.check()
