@@ -545,7 +545,9 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
         u.window_lo = kNoWindow;
         u.kv_lo = 0;
         if (cfg.window > 0) {
-          u.window_lo = r.kv_len - r.qo_len + t0 - cfg.window + 1;
+          // (in 64 bits: a window longer than every row reaches below kNoWindow)
+          const int64_t lo = static_cast<int64_t>(r.kv_len) - r.qo_len + t0 - cfg.window + 1;
+          u.window_lo = static_cast<int32_t>(std::max<int64_t>(lo, kNoWindow));
           u.kv_lo = std::min(std::max(u.window_lo, 0), std::max(end - 1, 0)) / kChunkGranule * kChunkGranule;
         }
         u.l_eff = std::max(end - u.kv_lo, 0);

@@ -28,6 +28,8 @@ CASES = [
     ("win_mfma_d256_causal_split", [90, 17], [600, 17], 16, 4, 256, 1, "bf16", True, 0.0, 8, 77),
     ("win_one_mfma", [70, 5], [70, 80], 8, 2, 128, 3, "bf16", True, 0.0, 0, 1),
     ("win_longer_than_kv", [40, 1], [100, 64], 8, 2, 128, 16, "bf16", True, 0.0, 0, 5000),
+    # the largest window with more queries than keys (non-causal)
+    ("win_huge_noncausal", [129, 1], [65, 70], 8, 2, 128, 16, "bf16", False, 0.0, 0, 2**31 - 1),
 ]
 
 

@@ -279,6 +279,9 @@ WINDOW_CASES = [
     ("noncausal_window", [33, 1], [90, 450], 4, 1, 64, 2, "bf16", False, 5, 64),
     ("window_one", [5, 1, 2], [5, 70, 200], 4, 2, 64, 3, "bf16", True, 4, 1),
     ("window_covers_all", [3, 1], [50, 90], 4, 2, 64, 16, "bf16", True, 4, 1000),
+    ("window_empty_rows", [1, 0, 1, 2], [0, 5, 70, 0], 4, 2, 64, 4, "bf16", False, 4, 10),
+    # more queries than keys (non-causal) and the largest window: no int32 overflow
+    ("window_huge_noncausal", [9, 1], [4, 70], 4, 2, 64, 3, "bf16", False, 4, 2**31 - 1),
 ]
 
 
@@ -306,7 +309,7 @@ def test_window_plan_executes_to_oracle(case):
         r = int(np.searchsorted(qo_ptr, int(it["qo_begin"]), side="right")) - 1
         t0 = int(it["qo_begin"]) - int(qo_ptr[r])
         first = kv[r] - qo[r] + t0 - window + 1
-        assert int(it["window_lo"]) == first
+        assert int(it["window_lo"]) == max(first, -0x3FFFFFFF)
         assert int(it["kv_begin"]) >= max(first, 0) // 64 * 64, name
 
 
