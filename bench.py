@@ -268,6 +268,18 @@ def bench_append(name, steps, warmup, flush, mode="read"):
                               frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)), None
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if not readable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The oracle as it stands, on the full workload, repeated for about budget_s."""
     import threadpoolctl
@@ -295,6 +307,7 @@ def cpu_baseline(w, budget_s=10.0):
         value=work["bytes"] / dt / 1e12,
         unit="TB/s",
         cores=cores,
+        cpu_model=cpu_model(),
         kind="oracle",
         sample=f"whole {w.name} workload ({w.batch} requests, all heads), {reps} repetition(s), {dt:.2f} s each",
         seconds_per_step=dt,

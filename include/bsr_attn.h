@@ -150,7 +150,9 @@ typedef struct bsr_plan_info {
   int64_t max_wg_cost;     /* largest per-workgroup cost after assignment */
   int64_t total_cost;
   int32_t blob_bytes;      /* bytes of plan uploaded to the workspace */
-  int32_t reserved;
+  int32_t instance;        /* kernel instance the plan runs on (kind, decode rows, head dim,
+                              switches); plans with equal values and num_workgroups replay
+                              under one captured run */
 } bsr_plan_info;
 
 typedef struct bsr_attn* bsr_attn_t;
@@ -169,8 +171,9 @@ int bsr_attn_workspace_size(bsr_attn_t h, size_t* device_bytes, size_t* host_byt
  * the merge map, write the plan into host_staging and enqueue its copy into
  * workspace on stream.  Before rewriting host_staging it waits for the previous
  * copy from it.  Deterministic: the same lengths give the same plan bytes.
- * Not capturable in a HIP graph.  workspace may be NULL (then nothing is uploaded;
- * required for host-only handles).  Returns BSR_ERR_CAPACITY beyond the maxima,
+ * Not capturable in a HIP graph.  workspace may be NULL (then nothing is uploaded,
+ * and bsr_attn_run keeps launching the last plan that was; required for host-only
+ * handles).  Returns BSR_ERR_CAPACITY beyond the maxima,
  * BSR_ERR_INVALID_ARG for non-monotone indptrs, last_page_len outside [1, P] for a
  * non-empty row, or (causal) a row with l_qo > l_kv. */
 int bsr_attn_plan(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
@@ -188,19 +191,27 @@ int bsr_attn_plan_composable(bsr_attn_t h, int32_t num_formats, const bsr_format
 /* Statistics of the last plan made on this handle. */
 int bsr_attn_plan_get_info(bsr_attn_t h, bsr_plan_info* info);
 
-/* Run the last plan: one launch of the persistent kernel on stream (asynchronous).
- * q, k_pool, v_pool, kv_indices, o, lse (nullable) and workspace are device
- * pointers in the layouts above; kv_indices must be the array the plan's
- * kv_indptr (and format offsets) index, with page ids < the pool's page count
- * (caller contract, not checked).  No allocation, no synchronisation, constant
- * grid: capturable in a HIP graph; a captured run replays any later plan with the
- * same kernel kind (bsr_plan_info.kernel) and pointers. */
+/* Run the last plan uploaded to a workspace: one launch of the persistent kernel on
+ * stream (asynchronous).  q, k_pool, v_pool, kv_indices, o, lse (nullable) and
+ * workspace are device pointers in the layouts above; kv_indices must be the array
+ * the plan's kv_indptr (and format offsets) index, with page ids < the pool's page
+ * count (caller contract, not checked).  No allocation, no synchronisation,
+ * constant grid: capturable in a HIP graph.  A captured run replays any later plan
+ * uploaded to the same workspace whose bsr_plan_info.instance and num_workgroups
+ * equal those of the plan it was captured with (same pointers).  The instance
+ * changes with the kernel kind and, for the decode and mixed kinds, with the
+ * decode body's folded rows: 4 when every block row folds into at most 4 rows
+ * (l_qo * g <= 4), else 8.  A replay that meets a plan made for another instance
+ * or grid computes nothing and writes no output; bsr_attn_check then returns
+ * BSR_ERR_DEVICE. */
 int bsr_attn_run(bsr_attn_t h, const void* q, const void* k_pool, const void* v_pool,
                  const int32_t* kv_indices, void* o, float* lse, void* workspace,
                  void* stream);
 
 /* Synchronise stream and report whether the device flagged an error during the
- * runs since the last plan (a bounded wait that expired).  BSR_OK if none. */
+ * runs since the last upload: a bounded wait for a partial state that expired, or
+ * a launch that met a plan made for another kernel instance or grid
+ * (BSR_ERR_DEVICE).  BSR_OK if none. */
 int bsr_attn_check(bsr_attn_t h, void* workspace, void* stream);
 
 /* Stand-alone ⊕ of two sets of attention states (Terms "Attention State and ⊕"):

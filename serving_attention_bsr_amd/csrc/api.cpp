@@ -99,8 +99,11 @@ struct bsr_attn {
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
   bool has_plan = false;
-  PlanResult last;
+  PlanResult last;  // the last plan made (reported by plan_get_info)
+  // the last plan uploaded into a workspace: what run() launches
+  bool has_upload = false;
   int32_t off_status = 0;
+  int32_t run_wg = 0;
   const void* kernel = nullptr;
   bsr::RunParams params;
 };
@@ -232,6 +235,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.page_size = cfg->page_size;
   pc.causal = cfg->causal != 0;
   pc.bf16 = bf16;
+  pc.cap = cap;
   pc.kv8 = kv8;
   for (int k = 0; k < 4; ++k) pc.num_wg[k][0] = h->num_wg[k][0], pc.num_wg[k][1] = h->num_wg[k][1];
   pc.alpha = cfg->cost_alpha > 0 ? cfg->cost_alpha : 1;
@@ -249,12 +253,13 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.max_total_qo = cfg->max_total_qo;
   pc.max_total_kv = cfg->max_total_kv;
   // partial states: at most 2 * #WG chunks of split units, each at most one tile
-  // of folded rows (paper Appendix D.3), plus one state per format for tokens of
-  // composed formats
+  // of folded rows (paper Appendix D.3), plus, for composed formats, one state per
+  // format for every query token and query head (two formats: the shared-prefix
+  // case; more formats need max_partial_rows)
   const int64_t tile_max = bsr::mfma_tile(cfg->head_dim);
   pc.max_partial_rows = cfg->max_partial_rows > 0
                             ? cfg->max_partial_rows
-                            : 2LL * max_wg * tile_max + 2LL * cfg->max_total_qo * g;
+                            : 2LL * max_wg * tile_max + 2LL * cfg->max_total_qo * cfg->num_qo_heads;
   // plan segment: header, status, epochs, flags, queues, items, merge map
   const int64_t hk = cfg->num_kv_heads;
   const int64_t units = hk * (2LL * cfg->max_batch + (int64_t(cfg->max_total_qo) * g + 31) / 32);
@@ -337,10 +342,15 @@ static int finish_plan(bsr_attn_t h, std::vector<BlockRow>& rows, int32_t total_
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     h->upload_pending = true;
   }
-  bsr::PlanHeader hdr;
-  std::memcpy(&hdr, res.blob.data(), sizeof(hdr));
-  h->off_status = hdr.off_status;
-  h->kernel = fn;
+  if (workspace != nullptr) {
+    // run() launches what the workspace holds: only an uploaded plan changes it
+    bsr::PlanHeader hdr;
+    std::memcpy(&hdr, res.blob.data(), sizeof(hdr));
+    h->off_status = hdr.off_status;
+    h->kernel = fn;
+    h->run_wg = res.num_wg;
+    h->has_upload = true;
+  }
   h->last = std::move(res);
   h->has_plan = true;
   return BSR_OK;
@@ -448,6 +458,9 @@ int bsr_attn_plan_get_info(bsr_attn_t h, bsr_plan_info* info) {
   info->max_wg_cost = r.max_wg_cost;
   info->total_cost = r.total_cost;
   info->blob_bytes = static_cast<int32_t>(r.blob.size());
+  bsr::PlanHeader hdr;
+  std::memcpy(&hdr, r.blob.data(), sizeof(hdr));
+  info->instance = hdr.instance;
   return BSR_OK;
 }
 
@@ -455,7 +468,7 @@ int bsr_attn_run(bsr_attn_t h, const void* q, const void* k_pool, const void* v_
                  const int32_t* kv_indices, void* o, float* lse, void* workspace, void* stream) {
   if (h == nullptr) return fail(BSR_ERR_INVALID_ARG, "handle is null");
   if (h->device < 0) return fail(BSR_ERR_INVALID_ARG, "a host-only handle cannot run");
-  if (!h->has_plan) return fail(BSR_ERR_INVALID_ARG, "run before any plan");
+  if (!h->has_upload) return fail(BSR_ERR_INVALID_ARG, "run before any plan was uploaded to a workspace");
   if (q == nullptr || k_pool == nullptr || v_pool == nullptr || kv_indices == nullptr || o == nullptr ||
       workspace == nullptr)
     return fail(BSR_ERR_INVALID_ARG, "null device pointer");
@@ -470,7 +483,7 @@ int bsr_attn_run(bsr_attn_t h, const void* q, const void* k_pool, const void* v_
   p.lse = lse;
   p.ws = static_cast<uint8_t*>(workspace);
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(h->kernel, dim3(static_cast<uint32_t>(h->last.num_wg)),
+  hipError_t e = hipLaunchKernel(h->kernel, dim3(static_cast<uint32_t>(h->run_wg)),
                                  dim3(bsr::kWgThreads), args, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hipLaunchKernel");
   return BSR_OK;
@@ -479,7 +492,7 @@ int bsr_attn_run(bsr_attn_t h, const void* q, const void* k_pool, const void* v_
 int bsr_attn_check(bsr_attn_t h, void* workspace, void* stream) {
   if (h == nullptr || workspace == nullptr) return fail(BSR_ERR_INVALID_ARG, "null argument");
   if (h->device < 0) return fail(BSR_ERR_INVALID_ARG, "a host-only handle has no device state");
-  if (!h->has_plan) return BSR_OK;
+  if (!h->has_upload) return BSR_OK;
   DeviceGuard guard(h->device);
   if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -488,6 +501,10 @@ int bsr_attn_check(bsr_attn_t h, void* workspace, void* stream) {
   int32_t status[4] = {0, 0, 0, 0};
   e = hipMemcpy(status, static_cast<uint8_t*>(workspace) + h->off_status, sizeof(status), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  if (status[bsr::kStatusWrongKernel] != 0)
+    return fail(BSR_ERR_DEVICE,
+                "the workspace holds a plan made for another kernel instance or grid than the one launched "
+                "(a captured run replayed after a plan that needs a different instance); nothing was computed");
   if (status[bsr::kStatusWaitTimeout] != 0)
     return fail(BSR_ERR_DEVICE, "a merge task gave up waiting for a partial state (workgroups not co-resident?)");
   return BSR_OK;

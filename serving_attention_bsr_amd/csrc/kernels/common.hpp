@@ -167,7 +167,6 @@ __device__ __forceinline__ int32_t* plan_i32(uint8_t* ws, int32_t off) {
   return reinterpret_cast<int32_t*>(ws + off);
 }
 
-constexpr int kMaxSpins = 1 << 21;
 
 // Load of memory that no thread writes during the kernel (the plan's queues),
 // through the constant address space: uniform reads become scalar loads, which
@@ -205,12 +204,13 @@ __device__ __forceinline__ float4 load_dev_f32x4(const float* p) {
                      __uint_as_float(static_cast<uint32_t>(b)), __uint_as_float(static_cast<uint32_t>(b >> 32)));
 }
 
-// Wait (bounded) until *flag == epoch.  Returns false if the bound expired.
-__device__ __forceinline__ bool wait_flag(const int32_t* flag, int32_t epoch) {
+// Wait (bounded) until *flag == epoch: at most spin_limit polls.  Returns false if
+// the bound expired.
+__device__ __forceinline__ bool wait_flag(const int32_t* flag, int32_t epoch, int32_t spin_limit) {
   int spins = 0;
   while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
     __builtin_amdgcn_s_sleep(2);
-    if (++spins > kMaxSpins) return false;
+    if (++spins > spin_limit) return false;
   }
   return true;
 }

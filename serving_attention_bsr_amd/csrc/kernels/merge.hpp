@@ -42,10 +42,10 @@ struct MergeBody {
   // Wait (bounded) for the ready stamps of a task's sources, one thread per
   // source; false if one never came.  All threads of the workgroup take part.
   static __device__ bool wait(const MergeTask& t, const MergeSrc* srcs, const int32_t* flags,
-                              int32_t epoch) {
+                              int32_t epoch, int32_t spin_limit) {
     bool ok = true;
     for (int s = threadIdx.x; s < t.src_count; s += kWgThreads)
-      if (ok) ok = wait_flag(flags + srcs[t.src_begin + s].flag_id, epoch);
+      if (ok) ok = wait_flag(flags + srcs[t.src_begin + s].flag_id, epoch, spin_limit);
     return ok;
   }
 

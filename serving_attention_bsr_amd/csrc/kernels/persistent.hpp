@@ -93,11 +93,19 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   asm volatile("" ::"s"(h.off_epochs), "s"(h.off_item_ptr), "s"(h.off_items), "s"(h.off_flags));
   const PlanHeader* hdr = &h;
   const int wg = blockIdx.x;
-  if (wg >= hdr->num_wg) return;  // grid larger than this plan's (never by construction)
+  int32_t* status = plan_i32(ws, hdr->off_status);
+  // A plan made for another instance (kind, decode rows, head dim, switches) or
+  // another grid is refused as a whole: nothing is written but the status word,
+  // which the host's check reports.  This is what a captured launch meets when a
+  // later plan needs a different instance.
+  constexpr int32_t kKey = instance_key(KIND, KIND == kKindMfma ? 0 : ROWS, D, BF16, CAP, PAGE1, KV8);
+  if (hdr->instance != kKey || hdr->num_wg != static_cast<int32_t>(gridDim.x)) {
+    if (wg == 0 && threadIdx.x == 0) status[kStatusWrongKernel] = 1;
+    return;
+  }
 
   int32_t* epochs = plan_i32(ws, hdr->off_epochs);
   int32_t* flags = plan_i32(ws, hdr->off_flags);
-  int32_t* status = plan_i32(ws, hdr->off_status);
   BSR_STAMP(0);
   // the run counter is first needed after the attention items: its (uniform) load
   // is issued here and waited for there, off the items' latency chain
@@ -150,7 +158,12 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   BSR_STAMP(1);
   // Stamps for the partial states this workgroup wrote: every wavefront waits
   // until its device-scope stores have completed (vector memory counter at 0),
-  // the workgroup meets, and wavefront 0 stores the stamps.
+  // the workgroup meets, and wavefront 0 stores the stamps.  This is the
+  // agent-scope release sequence of the AMDGPU memory model (wait for the vector
+  // memory counter, then store the flag) without its write-back of the L2 cache,
+  // which only data written into the L2 by non-atomic stores needs: every store of
+  // a partial state above must stay an agent-scope atomic store, and the merge's
+  // reads agent-scope atomic loads (the acquire side without the L2 invalidate).
   if (any_partial) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   // device-scope loads, so no cache of this XCD can hold them stale)
   bool ok = true;
   if (mb < me) {
-    for (int32_t t = mb; t < me && ok; ++t) ok = K::Merge::wait(tasks[t], srcs, flags, epoch);
+    for (int32_t t = mb; t < me && ok; ++t) ok = K::Merge::wait(tasks[t], srcs, flags, epoch, hdr->spin_limit);
     BSR_STAMP(3);
     __syncthreads();
     BSR_STAMP(5);

@@ -15,7 +15,7 @@
 //   [partial_lse_offset, ...)          fp32 [max_partial_rows] partial log2-sum-exp
 //
 // Plan blob (offsets inside the blob are in the header; all 16-byte aligned):
-//   PlanHeader
+//   PlanHeader       magic, kernel instance, counts, offsets, wait bound
 //   status[4]        device error words, zeroed by each upload
 //   epochs[num_wg]   per-workgroup run counters (all equal between runs)
 //   flags[num_flags] per-partial ready stamps (the epoch of the run that wrote it)
@@ -44,8 +44,24 @@ enum ItemFlags : int32_t {
 };
 
 enum StatusWord : int32_t {
-  kStatusWaitTimeout = 0,  // a merge gave up waiting for a partial
+  kStatusWaitTimeout = 0,    // a merge gave up waiting for a partial
+  kStatusWrongKernel = 1,    // the plan was made for another kernel instance or grid
 };
+
+// Identity of the persistent-kernel instance a plan is made for: the kernel kind,
+// the decode body's folded rows (0 for the MFMA-only kind), the head dim, and the
+// handle-level switches that select an instance.  The planner writes it into the
+// header and the kernel compares it with its own template arguments, so a launch
+// captured for one instance never runs a later plan made for another (for
+// example a decode graph captured at 4 folded rows replaying an 8-row plan).
+constexpr int32_t instance_key(int kind, int rows, int head_dim, bool bf16, bool cap, bool page1, bool kv8) {
+  return kind | (rows << 4) | ((head_dim / 64) << 8) | (bf16 ? 1 << 12 : 0) | (cap ? 1 << 13 : 0) |
+         (page1 ? 1 << 14 : 0) | (kv8 ? 1 << 15 : 0);
+}
+
+// Default bound of a merge's wait for one ready stamp, in polls (each poll sleeps
+// briefly); the planner writes it into the header.
+constexpr int32_t kDefaultSpinLimit = 1 << 21;
 
 struct WorkItem {  // 48 bytes
   int32_t flags;
@@ -74,7 +90,7 @@ struct MergeSrc {  // 8 bytes
   int32_t flag_id;      // ready flag of the item that wrote it
 };
 
-struct PlanHeader {  // 64 bytes
+struct PlanHeader {  // 80 bytes
   int32_t magic;
   int32_t kernel;
   int32_t num_wg;
@@ -91,11 +107,14 @@ struct PlanHeader {  // 64 bytes
   int32_t off_merge;
   int32_t off_srcs;
   int32_t blob_bytes;
+  int32_t instance;    // instance_key() of the kernel this plan is made for
+  int32_t spin_limit;  // polls before a merge gives up on a ready stamp
+  int32_t reserved[2];
 };
 
 static_assert(sizeof(WorkItem) == 48, "WorkItem layout");
 static_assert(sizeof(MergeTask) == 16, "MergeTask layout");
 static_assert(sizeof(MergeSrc) == 8, "MergeSrc layout");
-static_assert(sizeof(PlanHeader) == 64, "PlanHeader layout");
+static_assert(sizeof(PlanHeader) == 80, "PlanHeader layout");
 
 }  // namespace bsr

@@ -627,6 +627,9 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   hdr.num_merge = static_cast<int32_t>(tasks.size());
   hdr.num_srcs = static_cast<int32_t>(srcs.size());
   hdr.num_flags = num_flags;
+  hdr.instance = instance_key(kernel, kernel == kKindMfma ? 0 : decode_rows, cfg.head_dim, cfg.bf16, cfg.cap,
+                              kernel == kKindMfma && cfg.page_size == 1, cfg.kv8);
+  hdr.spin_limit = kDefaultSpinLimit;
   int64_t off = sizeof(PlanHeader);
   hdr.off_status = align16(off);
   off = hdr.off_status + 16;

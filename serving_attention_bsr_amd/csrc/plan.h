@@ -19,6 +19,7 @@ struct PlanConfig {
   int32_t h_qo = 0, h_kv = 0, group = 0, head_dim = 0, page_size = 0;
   bool causal = false;
   bool bf16 = false;
+  bool cap = false;  // logits soft-cap on (selects the kernel instance)
   // grid per kernel instance: [KernelKind][decode rows 4 -> 0, 8 -> 1]
   int32_t num_wg[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
   int64_t alpha = 1, beta = 1;

@@ -104,11 +104,11 @@ class bsr_plan_info(ctypes.Structure):
         ("max_wg_cost", ctypes.c_int64),
         ("total_cost", ctypes.c_int64),
         ("blob_bytes", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("instance", ctypes.c_int32),
     ]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 _lib = None

@@ -1,7 +1,7 @@
 """Decoder of the plan bytes a host-only handle stages, and a CPU float64 executor.
 
 The layout decoded here is the one documented in the library's layout header:
-a 64-byte header of int32 offsets, then status words, per-workgroup epochs,
+an 80-byte header of int32 counts, offsets, the kernel instance and the wait bound, then status words, per-workgroup epochs,
 ready flags, per-workgroup item queues (CSR), 48-byte work items, per-workgroup
 merge queues (CSR), 16-byte merge tasks and 8-byte merge sources.
 
@@ -19,8 +19,9 @@ import oracle
 HEADER_FIELDS = [
     "magic", "kernel", "num_wg", "num_items", "num_merge", "num_srcs", "num_flags",
     "off_status", "off_epochs", "off_flags", "off_item_ptr", "off_items", "off_merge_ptr",
-    "off_merge", "off_srcs", "blob_bytes",
+    "off_merge", "off_srcs", "blob_bytes", "instance", "spin_limit", "reserved0", "reserved1",
 ]
+HEADER_BYTES = 4 * len(HEADER_FIELDS)
 ITEM = np.dtype([
     ("flags", "<i4"), ("qo_begin", "<i4"), ("qo_count", "<i4"), ("kv_head", "<i4"),
     ("page_begin", "<i4"), ("kv_begin", "<i4"), ("kv_end", "<i4"), ("causal_limit", "<i4"),
@@ -35,7 +36,7 @@ MAGIC = 0x41525342
 
 def decode(blob: np.ndarray) -> dict:
     blob = np.asarray(blob, dtype=np.uint8)
-    hdr = dict(zip(HEADER_FIELDS, np.frombuffer(blob[:64].tobytes(), dtype="<i4").tolist()))
+    hdr = dict(zip(HEADER_FIELDS, np.frombuffer(blob[:HEADER_BYTES].tobytes(), dtype="<i4").tolist()))
     assert hdr["magic"] == MAGIC
     nwg = hdr["num_wg"]
 

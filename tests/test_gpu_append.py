@@ -6,7 +6,7 @@ one key per page, a ragged mix with an empty request and a request with more new
 rows than positions, D = 256 with an odd page size, a long prefill whose rows
 cross requests inside one wavefront's range (more rows than wavefronts), and
 page ids outside the pool
-(those rows must not be written).  Pools start with random values everywhere, so
+(those rows must not be written), and FP8 (E4M3) caches.  Pools start with random values everywhere, so
 any write outside the expected slots shows up.
 """
 
@@ -28,6 +28,11 @@ CASES = [
     # more new rows than the grid has wavefronts (65536): each wavefront walks two
     # tokens, across request boundaries
     ("many_tokens_h1", [30000, 25001, 19999], [30000, 25001, 19999], 1, 64, 16, "bf16", 6),
+    # FP8 (E4M3) cache: one byte per element, 16-byte pieces of 16 elements
+    ("fp8_decode_p16", [int(x) for x in np.random.default_rng(7).integers(1, 300, 16)], [1] * 16, 8, 128, 16, "fp8",
+     7),
+    ("fp8_prefill_p1_d64", [5, 100, 33], [5, 100, 33], 4, 64, 1, "fp8", 8),
+    ("fp8_ragged_d256_p5_overflow", [10, 4, 0, 47], [3, 6, 0, 17], 2, 256, 5, "fp8", 9),
 ]
 
 
@@ -40,7 +45,7 @@ def _case(lens, new, h_kv, d, page_size, dtype, seed, spare=3):
     kv_indices = order[: sum(n_pages)].astype(np.int32)
     last = np.array([l - (n - 1) * page_size if n > 0 else page_size for l, n in zip(lens, n_pages)], dtype=np.int32)
     append_indptr = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}[dtype]
     g = torch.Generator().manual_seed(seed)
     k_pool = torch.randn((num_pages, h_kv, page_size, d), generator=g).to(tdt)
     v_pool = torch.randn((num_pages, h_kv, page_size, d), generator=g).to(tdt)
@@ -50,7 +55,8 @@ def _case(lens, new, h_kv, d, page_size, dtype, seed, spare=3):
 
 
 def _bits(t):
-    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).numpy()
+    view = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.float8_e4m3fn: torch.uint8}[t.dtype]
+    return t.view(view).numpy()
 
 
 def _gpu_append(k_pool, v_pool, k_new, v_new, append_indptr, kv_indptr, kv_indices, last):
