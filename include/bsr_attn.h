@@ -208,10 +208,28 @@ int bsr_attn_run(bsr_attn_t h, const void* q, const void* k_pool, const void* v_
                  const int32_t* kv_indices, void* o, float* lse, void* workspace,
                  void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): bsr_attn_run without a
+ * workspace argument.  The workspace is a static device array of the library,
+ * 64 MiB per device, held until the process ends; a handle whose
+ * bsr_attn_workspace_size device bytes exceed it is rejected with
+ * BSR_ERR_CAPACITY (lower max_partial_rows or the other maxima).  Each call copies
+ * the plan that the handle's last plan call wrote to host_staging (which must be
+ * that buffer; plan with a null workspace to skip the ordinary upload) into the
+ * array, which also clears every word that must start at zero, and launches the
+ * kernel on it: asynchronous on stream; no allocation.  All calls on one device
+ * share its array: calls that overlap on one device (several streams or handles)
+ * race.  bsr_attn_check with a null workspace reports the errors of these runs.
+ * Under graph capture each replay copies host_staging's contents at replay time. */
+int bsr_attn_run_static(bsr_attn_t h, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* kv_indices, void* o, float* lse, const void* host_staging,
+                        void* stream);
+
 /* Synchronise stream and report whether the device flagged an error during the
  * runs since the last upload: a bounded wait for a partial state that expired, or
  * a launch that met a plan made for another kernel instance or grid
- * (BSR_ERR_DEVICE).  BSR_OK if none. */
+ * (BSR_ERR_DEVICE).  BSR_OK if none.  A null workspace checks the runs of
+ * bsr_attn_run_static instead. */
 int bsr_attn_check(bsr_attn_t h, void* workspace, void* stream);
 
 /* Stand-alone ⊕ of two sets of attention states (Terms "Attention State and ⊕"):

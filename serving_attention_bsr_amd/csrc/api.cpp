@@ -14,12 +14,17 @@
 #include <vector>
 
 #include "bsr_attn.h"
+#include "handle.h"
 #include "kernels/registry.h"
 #include "layout.h"
 #include "params.h"
 #include "plan.h"
 
 using bsr::BlockRow;
+using bsr::align_up;
+using bsr::DeviceGuard;
+using bsr::fail;
+using bsr::hip_fail;
 using bsr::KernelKey;
 using bsr::PlanConfig;
 using bsr::PlanResult;
@@ -28,7 +33,8 @@ using bsr::PlanResult;
 // sixteenths of the first's (from a sweep on MI355X; see the planner).
 constexpr int32_t kSlot2Speed16 = 11;
 
-namespace {
+
+namespace bsr {
 
 thread_local std::string g_error;
 
@@ -41,31 +47,6 @@ int hip_fail(hipError_t e, const char* what) {
   g_error = std::string(what) + ": " + hipGetErrorString(e);
   return BSR_ERR_HIP;
 }
-
-int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
-
-// Makes a device current for the duration of a call, then restores the caller's.
-struct DeviceGuard {
-  int prev = -1;
-  bool active = false;
-  hipError_t err = hipSuccess;
-  explicit DeviceGuard(int dev) {
-    if (dev < 0) return;
-    err = hipGetDevice(&prev);
-    if (err != hipSuccess) return;
-    if (prev != dev) {
-      err = hipSetDevice(dev);
-      active = err == hipSuccess;
-    }
-  }
-  ~DeviceGuard() {
-    if (active) (void)hipSetDevice(prev);
-  }
-};
-
-}  // namespace
-
-namespace bsr {
 
 const void* find_kernel(const KernelKey& key, int* wg_per_cu) {
   static std::vector<KernelEntry> table;
@@ -88,25 +69,6 @@ const void* find_kernel(const KernelKey& key, int* wg_per_cu) {
 
 }  // namespace bsr
 
-struct bsr_attn {
-  bsr_attn_config cfg;
-  int device = -1;
-  int cus = 0;  // compute units of the device (0 for host-only handles)
-  PlanConfig pc;
-  int32_t num_wg[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};  // [kind][decode rows 4/8]
-  int64_t plan_capacity = 0;
-  int64_t partial_o_off = 0, partial_lse_off = 0, ws_bytes = 0;
-  hipEvent_t upload_done = nullptr;
-  bool upload_pending = false;
-  bool has_plan = false;
-  PlanResult last;  // the last plan made (reported by plan_get_info)
-  // the last plan uploaded into a workspace: what run() launches
-  bool has_upload = false;
-  int32_t off_status = 0;
-  int32_t run_wg = 0;
-  const void* kernel = nullptr;
-  bsr::RunParams params;
-};
 
 namespace {
 
@@ -154,7 +116,7 @@ extern "C" {
 
 int bsr_attn_abi_version(void) { return BSR_ATTN_ABI_VERSION; }
 
-const char* bsr_attn_last_error(void) { return g_error.c_str(); }
+const char* bsr_attn_last_error(void) { return bsr::g_error.c_str(); }
 
 int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   if (out == nullptr) return fail(BSR_ERR_INVALID_ARG, "out is null");
@@ -214,6 +176,16 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
         } else {
           h->num_wg[kind][ri] = std::min(per_cu, std::max(preferred, 1)) * cus;
         }
+      }
+    }
+    // the static scratch of bsr_attn_run_static: its device address is looked up
+    // once per device, here, with the device current
+    {
+      uint8_t* scratch = nullptr;
+      int64_t scratch_bytes = 0;
+      if (int rc = bsr::static_scratch(device, &scratch, &scratch_bytes)) {
+        delete h;
+        return rc;
       }
     }
     e = hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming);
@@ -334,6 +306,8 @@ static int finish_plan(bsr_attn_t h, std::vector<BlockRow>& rows, int32_t total_
     h->upload_pending = false;
   }
   std::memcpy(host_staging, res.blob.data(), res.blob.size());
+  h->last_staging = host_staging;
+  h->last_kernel = fn;
   if (workspace != nullptr) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(workspace, host_staging, res.blob.size(), hipMemcpyHostToDevice, s);
@@ -490,16 +464,24 @@ int bsr_attn_run(bsr_attn_t h, const void* q, const void* k_pool, const void* v_
 }
 
 int bsr_attn_check(bsr_attn_t h, void* workspace, void* stream) {
-  if (h == nullptr || workspace == nullptr) return fail(BSR_ERR_INVALID_ARG, "null argument");
+  if (h == nullptr) return fail(BSR_ERR_INVALID_ARG, "null argument");
   if (h->device < 0) return fail(BSR_ERR_INVALID_ARG, "a host-only handle has no device state");
-  if (!h->has_upload) return BSR_OK;
+  // a null workspace checks the runs of bsr_attn_run_static (the static scratch)
+  const bool scratch = workspace == nullptr;
+  if (scratch ? !h->has_static : !h->has_upload) return BSR_OK;
   DeviceGuard guard(h->device);
   if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  if (scratch) {
+    int64_t bytes = 0;
+    if (int rc = bsr::static_scratch(h->device, &base, &bytes)) return rc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   int32_t status[4] = {0, 0, 0, 0};
-  e = hipMemcpy(status, static_cast<uint8_t*>(workspace) + h->off_status, sizeof(status), hipMemcpyDeviceToHost);
+  e = hipMemcpy(status, base + (scratch ? h->static_off_status : h->off_status), sizeof(status),
+                hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
   if (status[bsr::kStatusWrongKernel] != 0)
     return fail(BSR_ERR_DEVICE,

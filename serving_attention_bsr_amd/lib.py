@@ -41,6 +41,7 @@ EXPORTED = [
     "bsr_attn_plan_composable",
     "bsr_attn_plan_get_info",
     "bsr_attn_run",
+    "bsr_attn_run_static",
     "bsr_attn_check",
     "bsr_attn_merge_states",
     "bsr_attn_append_kv",
@@ -134,6 +135,7 @@ def load():
     lib.bsr_attn_plan_composable.argtypes = [vp, c_i32, ctypes.POINTER(bsr_format), c_i32, vp, vp, vp]
     lib.bsr_attn_plan_get_info.argtypes = [vp, ctypes.POINTER(bsr_plan_info)]
     lib.bsr_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, f32p, vp, vp]
+    lib.bsr_attn_run_static.argtypes = [vp, vp, vp, vp, vp, vp, f32p, vp, vp]
     lib.bsr_attn_check.argtypes = [vp, vp, vp]
     lib.bsr_attn_merge_states.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p, c_i64, c_i32, vp]
     lib.bsr_attn_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, vp, vp,
@@ -224,6 +226,10 @@ def bsr_attn_plan_get_info(h):
 
 def bsr_attn_run(h, q, k_pool, v_pool, kv_indices, o, lse, workspace, stream):
     _check(load().bsr_attn_run(h, q, k_pool, v_pool, kv_indices, o, lse, workspace, stream))
+
+
+def bsr_attn_run_static(h, q, k_pool, v_pool, kv_indices, o, lse, host_staging, stream):
+    _check(load().bsr_attn_run_static(h, q, k_pool, v_pool, kv_indices, o, lse, host_staging, stream))
 
 
 def bsr_attn_check(h, workspace, stream):
@@ -327,8 +333,11 @@ class BsrAttention:
 
         return _stream_ptr(torch.cuda.current_stream(self.device))
 
-    def plan(self, qo_indptr, kv_indptr, last_page_len):
-        bsr_attn_plan(self.handle, qo_indptr, kv_indptr, last_page_len, self._ws_ptr, self._staging_ptr, self._stream())
+    def plan(self, qo_indptr, kv_indptr, last_page_len, upload=True):
+        """upload=False stages the plan without copying it into the workspace (for
+        run_static, which uploads it into the library's static scratch)."""
+        ws = self._ws_ptr if upload else None
+        bsr_attn_plan(self.handle, qo_indptr, kv_indptr, last_page_len, ws, self._staging_ptr, self._stream())
         return self.info()
 
     def plan_composable(self, formats, total_qo):
@@ -358,8 +367,23 @@ class BsrAttention:
         )
         return o, lse
 
-    def check(self):
-        bsr_attn_check(self.handle, self._ws_ptr, self._stream())
+    def run_static(self, q, k_pool, v_pool, kv_indices, o=None, lse=None):
+        """run() on the library's static scratch instead of this object's workspace."""
+        import torch
+
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+        bsr_attn_run_static(
+            self.handle, _dptr(q), _dptr(k_pool), _dptr(v_pool), _dptr(kv_indices), _dptr(o), _dptr(lse),
+            self._staging_ptr, self._stream(),
+        )
+        return o, lse
+
+    def check(self, static=False):
+        """static=True checks the runs of run_static (the static scratch)."""
+        bsr_attn_check(self.handle, None if static else self._ws_ptr, self._stream())
 
     def close(self):
         if self.handle is not None:
