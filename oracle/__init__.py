@@ -16,3 +16,4 @@ from .attention import (  # noqa: F401
 )
 from .append import append_paged_kv, append_slots  # noqa: F401
 from .fp8 import decode_e4m3  # noqa: F401
+from .quest import page_scores, page_summaries, quest_attention, quest_selection, select_pages  # noqa: F401

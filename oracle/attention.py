@@ -21,7 +21,8 @@ Sources (the FlashInfer explainer page on zenmind.me, "FlashInferï¼šé¢å‘ LLM æ
   * Background, challenge 2 (paper section 1): logits soft-cap as a custom score.
   * Section "Reproduction" (paper section 4.2): prefill is run with a causal mask.
   * Background, "variants" (paper sections 1 and 3.2.3): masks such as a sliding
-    window are one of the variant axes (the LogitsMask functor).
+    window and ALiBi are variant axes (the LogitsMask and LogitsTransform
+    functors); Quick read item 1 names custom masks for speculative decoding.
 
 What this oracle computes is the plain definition of attention, with no tiling,
 online softmax, chunking or plan:
@@ -39,6 +40,15 @@ Readings where the pages are silent (each is listed in the design notes):
     query token t sees keys j > l_kv - l_qo + t - W, that is the W keys ending at
     its own position when the mask is also causal.  The window bounds keys from
     below only; the causal flag bounds them from above.
+  * ALiBi (the pages name it, do not define it): query head h has a slope m_h
+    (given by the caller) and its logit for key j gains m_h * (j - p), where p is
+    the query's bottom-right aligned position l_kv - l_qo + t.  The bias is added to
+    the scaled logit, before the soft-cap and the masks.
+  * Tree masks for speculative decoding (named, not defined): the l_qo new tokens
+    of a request are its last l_qo keys; a boolean matrix M [l_qo, l_qo] per
+    request lets token t see key l_kv - l_qo + u iff M[t, u]; keys before the new
+    tokens stay visible.  The tree mask applies on top of the causal and window
+    masks.
   * Query head h reads KV head floor(h / g).
   * A request with n pages holds l_kv = (n - 1) * P + last_page_len tokens; a
     request with no pages, and a row whose every key is masked, give O = 0 and
@@ -94,13 +104,15 @@ def gather_request_kv(pool, kv_indptr, kv_indices, last_page_len, r, page_size):
     return np.asarray(pool[pages, :, tau % page_size, :], dtype=np.float64)
 
 
-def attention_dense(q, k, v, scale, cap=0.0, visible=None, lowest=None):
+def attention_dense(q, k, v, scale, cap=0.0, visible=None, lowest=None, bias=None, allowed=None):
     """Attention state (O, LSE) of query rows q against keys k and values v.
 
     q: [n, D], k and v: [L, D] (float64).  visible: None (every key visible) or an
     int array [n] giving, per query row, the largest visible key index (keys
     j > visible[i] are masked); lowest: None or an int array [n] giving the
-    smallest visible key index (keys j < lowest[i] are masked).  Returns O [n, D]
+    smallest visible key index (keys j < lowest[i] are masked); bias: None or an
+    [n, L] array added to the scaled logits before the cap (ALiBi); allowed: None
+    or a boolean [n, L] array, False masks the key (tree masks).  Returns O [n, D]
     and LSE [n] (natural log).
 
     The state definition is the one of Terms, "Attention State and âŠ•" (paper
@@ -116,6 +128,8 @@ def attention_dense(q, k, v, scale, cap=0.0, visible=None, lowest=None):
     if n == 0 or length == 0:
         return out, lse
     s = scale * (q @ k.T)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)
     if cap > 0.0:
         s = cap * np.tanh(s / cap)
     if visible is not None:
@@ -124,6 +138,8 @@ def attention_dense(q, k, v, scale, cap=0.0, visible=None, lowest=None):
     if lowest is not None:
         cols = np.arange(length)[None, :]
         s = np.where(cols >= np.asarray(lowest)[:, None], s, -np.inf)
+    if allowed is not None:
+        s = np.where(np.asarray(allowed, dtype=bool), s, -np.inf)
     m = np.max(s, axis=1)
     live = np.isfinite(m)
     if not np.any(live):
@@ -152,6 +168,8 @@ def bsr_attention(
     causal=False,
     cap=0.0,
     window=0,
+    alibi_slopes=None,
+    tree_masks=None,
 ):
     """Attention of ragged queries over a BSR/paged KV cache.
 
@@ -162,7 +180,9 @@ def bsr_attention(
     mechanism 1; the GQA mapping follows Terms, "GQA head-group fusion"; the causal
     mask is the prefill mask of section "Reproduction" (paper section 4.2), aligned
     bottom-right as stated in the module notes; window > 0 adds the sliding-window
-    mask of the module notes.
+    mask of the module notes.  alibi_slopes ([H_qo] or None) adds the ALiBi bias
+    and tree_masks (per request a boolean [l_qo, l_qo] array, or None) the tree
+    mask of the module notes (Background, variants; paper section 3.2.3).
     """
     q = np.asarray(q)
     total, h_qo, d = q.shape
@@ -185,8 +205,18 @@ def bsr_attention(
         lowest = None
         if window > 0:
             lowest = l_kv - l_qo + np.arange(l_qo) - window + 1
+        allowed = None
+        if tree_masks is not None and tree_masks[r] is not None:
+            tree = np.asarray(tree_masks[r], dtype=bool)
+            assert tree.shape == (l_qo, l_qo) and l_kv >= l_qo, "a tree mask covers the request's new tokens"
+            allowed = np.ones((l_qo, l_kv), dtype=bool)
+            allowed[:, l_kv - l_qo :] = tree
+        positions = l_kv - l_qo + np.arange(l_qo)  # bottom-right aligned query positions
         for h in range(h_qo):
             hk = h // g
+            bias = None
+            if alibi_slopes is not None:
+                bias = float(alibi_slopes[h]) * (np.arange(l_kv)[None, :] - positions[:, None])
             o_h, lse_h = attention_dense(
                 np.asarray(q[q0:q1, h, :], dtype=np.float64),
                 k_r[:, hk, :],
@@ -195,6 +225,8 @@ def bsr_attention(
                 cap,
                 visible,
                 lowest,
+                bias,
+                allowed,
             )
             out[q0:q1, h, :] = o_h
             lse[q0:q1, h] = lse_h

@@ -18,7 +18,7 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "attent
 MUTANTS = {
     "page_slot_swapped": ("tau // page_size]", "tau % page_size]"),
     "last_page_len_ignored": ("l_kv = (n_pages - 1) * page_size + int(last_page_len[r])", "l_kv = n_pages * page_size"),
-    "gqa_modulo_mapping": ("hk = h // g\n            o_h, lse_h = attention_dense(\n                np.asarray(q[q0:q1, h, :]", "hk = h % num_kv_heads\n            o_h, lse_h = attention_dense(\n                np.asarray(q[q0:q1, h, :]"),
+    "gqa_modulo_mapping": ("hk = h // g\n            bias = None", "hk = h % num_kv_heads\n            bias = None"),
     "scale_dropped": ("s = scale * (q @ k.T)", "s = (q @ k.T)"),
     "k_transposed_with_v": ("out[live] = (w @ v) / z[:, None]", "out[live] = (w @ k) / z[:, None]"),
     "cap_factor_dropped": ("s = cap * np.tanh(s / cap)", "s = np.tanh(s / cap)"),
