@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define BSR_ATTN_ABI_VERSION 2
+#define BSR_ATTN_ABI_VERSION 3
 
 typedef enum bsr_status {
   BSR_OK = 0,
@@ -126,6 +126,13 @@ typedef struct bsr_attn_config {
                               (bsr_attn_plan_composable rejects it).  The planner gives
                               each query tile only the keys its window can reach */
   int32_t reserved;        /* must be 0 */
+  const float* alibi_slopes; /* NULL: no ALiBi.  Otherwise host array [num_qo_heads],
+                              read at create: query head h adds m_h * (j - p) to the
+                              scaled logit of key j before the soft-cap, p being the
+                              query's bottom-right aligned position l_kv - l_qo + t
+                              (ALiBi, one of the variants of the explainer page's
+                              Background and paper section 3.2.3); bsr_attn_plan and
+                              bsr_attn_plan_tree_mask only */
 } bsr_attn_config;
 
 /* One BSR sub-matrix for bsr_attn_plan_composable().  Arrays are host memory. */
@@ -180,10 +187,26 @@ int bsr_attn_plan(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indp
                   const int32_t* last_page_len, int32_t batch, void* workspace,
                   void* host_staging, void* stream);
 
+/* bsr_attn_plan with a tree mask over each block row's new tokens, for
+ * speculative decoding with a token tree (custom masks, Quick read item 1 and
+ * Background of the explainer page; paper section 3.2.3).  The l_qo query tokens
+ * of block row r are its last l_qo keys; token t sees key l_kv - l_qo + u only if
+ * bit (t, u) of the row's mask is set, and every earlier key as usual (the causal
+ * and window masks of the handle still apply).  tree_mask is a host bit array:
+ * block row r's l_qo x l_qo bits, row-major (bit t * l_qo + u), start at bit
+ * offset sum over r' < r of l_qo(r')^2, least significant bit first within each
+ * byte.  Returns BSR_ERR_UNSUPPORTED for a block row with more than 64 query
+ * tokens, BSR_ERR_INVALID_ARG for one with l_qo > l_kv or a null tree_mask, and
+ * otherwise behaves as bsr_attn_plan. */
+int bsr_attn_plan_tree_mask(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* last_page_len, int32_t batch, const uint8_t* tree_mask,
+                            void* workspace, void* host_staging, void* stream);
+
 /* Plan over several BSR sub-matrices of one KV matrix (Core mechanism 2).  A query
  * token's keys are the union of the keys of the block rows that cover it, in format
- * order; the formats must not overlap in keys (caller contract).  Causal handles
- * are not supported here.  Same staging/upload contract as bsr_attn_plan. */
+ * order; the formats must not overlap in keys (caller contract).  Causal, windowed
+ * and ALiBi handles are not supported here.  Same staging/upload contract as
+ * bsr_attn_plan. */
 int bsr_attn_plan_composable(bsr_attn_t h, int32_t num_formats, const bsr_format* formats,
                              int32_t total_qo, void* workspace, void* host_staging,
                              void* stream);

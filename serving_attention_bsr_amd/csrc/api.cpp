@@ -55,11 +55,14 @@ const void* find_kernel(const KernelKey& key, int* wg_per_cu) {
     register_d64(&table);
     register_d128(&table);
     register_d256(&table);
+    register_d64_var(&table);
+    register_d128_var(&table);
+    register_d256_var(&table);
   });
   for (const KernelEntry& e : table) {
     const KernelKey& k = e.key;
     if (k.kind == key.kind && k.bf16 == key.bf16 && k.head_dim == key.head_dim &&
-        k.rows == key.rows && k.cap == key.cap && k.page1 == key.page1 && k.kv8 == key.kv8) {
+        k.rows == key.rows && k.cap == key.cap && k.page1 == key.page1 && k.kv8 == key.kv8 && k.var == key.var) {
       if (wg_per_cu != nullptr) *wg_per_cu = e.wg_per_cu;
       return e.fn;
     }
@@ -98,6 +101,9 @@ int validate_config(const bsr_attn_config* c) {
   if (c->slot2_speed > 64) return fail(BSR_ERR_INVALID_ARG, "slot2_speed too large");
   if (c->sliding_window < 0) return fail(BSR_ERR_INVALID_ARG, "sliding_window must be >= 0");
   if (c->reserved != 0) return fail(BSR_ERR_INVALID_ARG, "reserved must be 0");
+  if (c->alibi_slopes != nullptr)
+    for (int32_t hq = 0; hq < c->num_qo_heads; ++hq)
+      if (!std::isfinite(c->alibi_slopes[hq])) return fail(BSR_ERR_INVALID_ARG, "ALiBi slopes must be finite");
   return BSR_OK;
 }
 
@@ -155,9 +161,10 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
     const int cus = prop.multiProcessorCount;
     h->cus = cus;
     for (int kind = bsr::kKindDecode; kind <= bsr::kKindMixed; ++kind) {
-      for (int ri = 0; ri < 2; ++ri) {
-        KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : (ri == 0 ? 4 : 8), cap,
-                      kind == bsr::kKindMfma && cfg->page_size == 1, kv8};
+      for (int ri = 0; ri < 4; ++ri) {
+        const bool var = ri >= 2;
+        KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : (ri % 2 == 0 ? 4 : 8), cap,
+                      kind == bsr::kKindMfma && cfg->page_size == 1, kv8, var};
         int preferred = 1;
         const void* fn = bsr::find_kernel(key, &preferred);
         if (fn == nullptr) continue;  // instance not built for this configuration
@@ -171,10 +178,11 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
         // what stays resident; a caller's budget is capped per instance
         const int resident = per_cu * cus;
         if (resident <= 0) continue;
+        int32_t& nwg = h->num_wg[kind][ri % 2][var ? 1 : 0];
         if (cfg->num_workgroups > 0) {
-          h->num_wg[kind][ri] = std::min(cfg->num_workgroups, resident);
+          nwg = std::min(cfg->num_workgroups, resident);
         } else {
-          h->num_wg[kind][ri] = std::min(per_cu, std::max(preferred, 1)) * cus;
+          nwg = std::min(per_cu, std::max(preferred, 1)) * cus;
         }
       }
     }
@@ -194,10 +202,12 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
       return hip_fail(e, "hipEventCreateWithFlags");
     }
   } else {
-    for (int kind = 1; kind <= 3; ++kind) h->num_wg[kind][0] = h->num_wg[kind][1] = cfg->num_workgroups;
+    for (int kind = 1; kind <= 3; ++kind)
+      for (int ri = 0; ri < 2; ++ri) h->num_wg[kind][ri][0] = h->num_wg[kind][ri][1] = cfg->num_workgroups;
   }
   int32_t max_wg = 1;
-  for (int kind = 1; kind <= 3; ++kind) max_wg = std::max({max_wg, h->num_wg[kind][0], h->num_wg[kind][1]});
+  for (int kind = 1; kind <= 3; ++kind)
+    for (int ri = 0; ri < 2; ++ri) max_wg = std::max({max_wg, h->num_wg[kind][ri][0], h->num_wg[kind][ri][1]});
 
   PlanConfig& pc = h->pc;
   pc.h_qo = cfg->num_qo_heads;
@@ -209,7 +219,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.bf16 = bf16;
   pc.cap = cap;
   pc.kv8 = kv8;
-  for (int k = 0; k < 4; ++k) pc.num_wg[k][0] = h->num_wg[k][0], pc.num_wg[k][1] = h->num_wg[k][1];
+  std::memcpy(pc.num_wg, h->num_wg, sizeof(pc.num_wg));
   pc.alpha = cfg->cost_alpha > 0 ? cfg->cost_alpha : 1;
   pc.beta = cfg->cost_beta > 0 ? cfg->cost_beta : 1;
   pc.min_chunk = cfg->min_kv_chunk > 0 ? cfg->min_kv_chunk : 64;
@@ -221,6 +231,14 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.cus = h->cus;
   pc.slot2_speed16 = cfg->slot2_speed > 0 ? cfg->slot2_speed : kSlot2Speed16;
   pc.window = cfg->sliding_window;
+  // ALiBi slopes in the units of the unscaled logit q.k: the kernels add
+  // (slope / sm_scale) * (j - p) before applying the scale
+  const float sm = cfg->sm_scale > 0.0f ? cfg->sm_scale : 1.0f / std::sqrt(float(cfg->head_dim));
+  if (cfg->alibi_slopes != nullptr) {
+    pc.alibi_raw.resize(cfg->num_qo_heads);
+    for (int32_t hq = 0; hq < cfg->num_qo_heads; ++hq) pc.alibi_raw[hq] = cfg->alibi_slopes[hq] / sm;
+  }
+  h->cfg.alibi_slopes = nullptr;  // read at create only
   pc.max_batch = cfg->max_batch;
   pc.max_total_qo = cfg->max_total_qo;
   pc.max_total_kv = cfg->max_total_kv;
@@ -238,10 +256,12 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   const int64_t max_items = units + 2LL * max_wg + 64;
   const int64_t max_tasks = int64_t(cfg->max_total_qo) * hk;
   const int64_t max_srcs = 2 * max_tasks + 2LL * max_wg * tile_max;
+  // (+ ALiBi slopes and one tree-mask row per query token)
   int64_t cap_bytes = sizeof(bsr::PlanHeader) + 16 + 4LL * max_wg + 4 * max_items +
                       2 * 4LL * (max_wg + 1) + int64_t(sizeof(bsr::WorkItem)) * max_items +
                       int64_t(sizeof(bsr::MergeTask)) * max_tasks +
-                      int64_t(sizeof(bsr::MergeSrc)) * max_srcs + 16 * 16;
+                      int64_t(sizeof(bsr::MergeSrc)) * max_srcs + 4LL * cfg->num_qo_heads +
+                      8LL * cfg->max_total_qo + 16 * 16;
   h->plan_capacity = align_up(cap_bytes, 256);
   pc.blob_capacity = h->plan_capacity;
   h->partial_o_off = h->plan_capacity;
@@ -281,20 +301,21 @@ int bsr_attn_workspace_size(bsr_attn_t h, size_t* device_bytes, size_t* host_byt
 }
 
 static int finish_plan(bsr_attn_t h, std::vector<BlockRow>& rows, int32_t total_qo, bool composable,
-                       void* workspace, void* host_staging, void* stream) {
+                       void* workspace, void* host_staging, void* stream,
+                       const std::vector<uint64_t>* tree_rows = nullptr) {
   if (host_staging == nullptr) return fail(BSR_ERR_INVALID_ARG, "host_staging is null");
   if (workspace != nullptr && h->device < 0)
     return fail(BSR_ERR_INVALID_ARG, "a host-only handle cannot upload to a workspace");
   PlanResult res;
   std::string err;
-  int rc = bsr::make_plan(h->pc, rows, total_qo, composable, &res, &err);
+  int rc = bsr::make_plan(h->pc, rows, total_qo, composable, &res, &err, tree_rows);
   if (rc != BSR_OK) return fail(rc, err);
   const int rows_key = res.kernel == bsr::kKindMfma ? 0 : res.decode_rows;
   const void* fn = nullptr;
   if (h->device >= 0) {
     fn = bsr::find_kernel(KernelKey{res.kernel, h->pc.bf16, h->pc.head_dim, rows_key,
                                     h->cfg.logits_soft_cap > 0.0f,
-                                    res.kernel == bsr::kKindMfma && h->pc.page_size == 1, h->pc.kv8});
+                                    res.kernel == bsr::kKindMfma && h->pc.page_size == 1, h->pc.kv8, res.var});
     if (fn == nullptr)
       return fail(BSR_ERR_UNSUPPORTED, "no kernel built for this plan's kind " + std::to_string(res.kernel));
   }
@@ -330,9 +351,10 @@ static int finish_plan(bsr_attn_t h, std::vector<BlockRow>& rows, int32_t total_
   return BSR_OK;
 }
 
-int bsr_attn_plan(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
-                  const int32_t* last_page_len, int32_t batch, void* workspace, void* host_staging,
-                  void* stream) {
+// Block rows of a single-format plan, validated (see bsr_attn_plan).
+static int single_format_rows(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                              const int32_t* last_page_len, int32_t batch, std::vector<BlockRow>* out,
+                              int32_t* total_qo_out) {
   if (h == nullptr) return fail(BSR_ERR_INVALID_ARG, "handle is null");
   if (batch < 0) return fail(BSR_ERR_INVALID_ARG, "batch must be >= 0");
   if (batch > h->cfg.max_batch) return fail(BSR_ERR_CAPACITY, "batch exceeds max_batch");
@@ -366,7 +388,46 @@ int bsr_attn_plan(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indp
   const int32_t total_qo = batch > 0 ? qo_indptr[batch] : 0;
   if (total_qo > h->cfg.max_total_qo) return fail(BSR_ERR_CAPACITY, "sum of query lengths exceeds max_total_qo");
   if (total_kv > h->cfg.max_total_kv) return fail(BSR_ERR_CAPACITY, "sum of KV lengths exceeds max_total_kv");
+  *out = std::move(rows);
+  *total_qo_out = total_qo;
+  return BSR_OK;
+}
+
+int bsr_attn_plan(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                  const int32_t* last_page_len, int32_t batch, void* workspace, void* host_staging,
+                  void* stream) {
+  std::vector<BlockRow> rows;
+  int32_t total_qo = 0;
+  if (int rc = single_format_rows(h, qo_indptr, kv_indptr, last_page_len, batch, &rows, &total_qo)) return rc;
   return finish_plan(h, rows, total_qo, false, workspace, host_staging, stream);
+}
+
+int bsr_attn_plan_tree_mask(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* last_page_len, int32_t batch, const uint8_t* tree_mask,
+                            void* workspace, void* host_staging, void* stream) {
+  std::vector<BlockRow> rows;
+  int32_t total_qo = 0;
+  if (int rc = single_format_rows(h, qo_indptr, kv_indptr, last_page_len, batch, &rows, &total_qo)) return rc;
+  if (batch > 0 && tree_mask == nullptr) return fail(BSR_ERR_INVALID_ARG, "tree_mask is null");
+  // one 64-bit row per query token: bit u = the token sees key l_kv - l_qo + u
+  std::vector<uint64_t> tree(total_qo, 0);
+  int64_t bit = 0;
+  for (int32_t r = 0; r < batch; ++r) {
+    BlockRow& br = rows[r];
+    const int32_t n = br.qo_len;
+    if (n > bsr::kMaxTreeTokens)
+      return fail(BSR_ERR_UNSUPPORTED, "block row " + std::to_string(r) + " has more than 64 tree-masked tokens");
+    if (n > br.kv_len)
+      return fail(BSR_ERR_INVALID_ARG, "block row " + std::to_string(r) + " has more tree tokens than keys");
+    br.tree = n > 0;
+    for (int32_t t = 0; t < n; ++t) {
+      uint64_t row = 0;
+      for (int32_t u = 0; u < n; ++u, ++bit)
+        if ((tree_mask[bit >> 3] >> (bit & 7)) & 1) row |= uint64_t(1) << u;
+      tree[br.qo_begin + t] = row;
+    }
+  }
+  return finish_plan(h, rows, total_qo, false, workspace, host_staging, stream, &tree);
 }
 
 int bsr_attn_plan_composable(bsr_attn_t h, int32_t num_formats, const bsr_format* formats,
@@ -375,6 +436,8 @@ int bsr_attn_plan_composable(bsr_attn_t h, int32_t num_formats, const bsr_format
   if (h->cfg.causal) return fail(BSR_ERR_UNSUPPORTED, "composed formats are not supported with causal masking");
   if (h->cfg.sliding_window > 0)
     return fail(BSR_ERR_UNSUPPORTED, "composed formats are not supported with a sliding window");
+  if (!h->pc.alibi_raw.empty())
+    return fail(BSR_ERR_UNSUPPORTED, "composed formats are not supported with ALiBi");
   if (num_formats < 1 || formats == nullptr) return fail(BSR_ERR_INVALID_ARG, "need at least one format");
   if (total_qo < 0 || total_qo > h->cfg.max_total_qo)
     return fail(total_qo < 0 ? BSR_ERR_INVALID_ARG : BSR_ERR_CAPACITY, "total_qo outside [0, max_total_qo]");

@@ -51,7 +51,7 @@ struct bsr_attn {
   int device = -1;
   int cus = 0;  // compute units of the device (0 for host-only handles)
   bsr::PlanConfig pc;
-  int32_t num_wg[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};  // [kind][decode rows 4/8]
+  int32_t num_wg[4][2][2] = {};  // [kind][decode rows 4/8][variant data]
   int64_t plan_capacity = 0;
   int64_t partial_o_off = 0, partial_lse_off = 0, ws_bytes = 0;
   hipEvent_t upload_done = nullptr;

@@ -159,6 +159,18 @@ __device__ __forceinline__ float pair_sum(float x) {
   return lo + hi;
 }
 
+// Variant data of one plan, read from its blob: ALiBi slopes per query head in
+// units of the unscaled logit (slope / sm_scale), and one 64-bit tree-mask row
+// per query token (bit u: the token sees key tree_lo + u of its block row).  An
+// absent array points at the start of the workspace instead of null, so that no
+// load, even one the compiler issues early, leaves valid memory (the workspace
+// holds at least 4 H_qo + 8 max_total_qo bytes).
+struct Variant {
+  bool has_alibi;
+  const float* alibi;
+  const uint64_t* tree;
+};
+
 // Workspace views.
 __device__ __forceinline__ const PlanHeader* plan_header(const uint8_t* ws) {
   return reinterpret_cast<const PlanHeader*>(ws);

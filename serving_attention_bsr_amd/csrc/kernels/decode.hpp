@@ -35,7 +35,9 @@ namespace bsr {
 // codes are converted exactly (E4M3 values are bf16 values) by the gfx950
 // conversion instruction, whose decoding of all 256 codes was checked against the
 // format on the GPU.
-template <int D, bool BF16, int ROWS, int TB, bool CAP, bool KV8 = false>
+// VAR: the plan may carry ALiBi slopes and tree masks (instances without it keep
+// the plain code, whose registers are tight).
+template <int D, bool BF16, int ROWS, int TB, bool CAP, bool KV8 = false, bool VAR = false>
 struct DecodeBody {
   static_assert(!KV8 || BF16, "an FP8 K/V cache has bf16 queries");
   static constexpr int LPT = D / 16;                 // lanes per KV row
@@ -96,6 +98,7 @@ struct DecodeBody {
     float m[ROWS];
     float l[ROWS];
   };
+
 
   // The state of the lane LEVEL lanes away in the ⊕ across lane groups, as a pair
   // (a, b) to be combined.  Below 16, a rotation by LEVEL within each 16 lanes (the
@@ -207,13 +210,27 @@ struct DecodeBody {
   // no-op (alpha = 1, p = 0 against finite values).
   static __device__ __forceinline__ void step(const RunParams& p, const WorkItem& it, int tile,
                                               int grp, bool live, const uint4 (&q)[ROWS][QLD],
-                                              const Kv& kv, State& st) {
+                                              const Kv& kv, const Variant& var, State& st) {
     float s[TB][ROWS];
 #pragma unroll
     for (int i = 0; i < TB; ++i)
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) s[i][r] = group_sum<LPT>(dot_row(q[r], kv.k[i]));
     const int g = p.group;
+    const int step_base = it.kv_begin + tile * TILE;
+    // ALiBi: key tau of row r (head kv_head g + r % g, token r / g) gains
+    // slope (tau - pos), before the soft-cap; the slopes are read here (uniform
+    // loads) rather than held for the whole item
+    if (VAR && var.has_alibi) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const float slope = load_invariant(var.alibi + it.kv_head * g + r % g);
+        const int pos = it.q_pos + r / g;
+#pragma unroll
+        for (int i = 0; i < TB; ++i)
+          s[i][r] = __builtin_fmaf(slope, static_cast<float>(step_base + i * NG + grp - pos), s[i][r]);
+      }
+    }
     // logits in base 2 are c * s: without a soft-cap the scale is folded into the
     // exponent's fma (c > 0, so the maximum of the raw scores gives the maximum);
     // with one, s is first mapped to cap * tanh(s / cap) in base 2
@@ -225,19 +242,23 @@ struct DecodeBody {
         for (int r = 0; r < ROWS; ++r) s[i][r] = p.cap_log2 * tanh_exp(s[i][r] * p.sm_scale * p.cap_inv);
     }
     // masks only on steps that reach past the chunk end or the causal limit of the
-    // first row, or below the sliding-window start of the last token (a real
-    // branch: most steps lie inside)
-    const int step_base = it.kv_begin + tile * TILE;
+    // first row, below the sliding-window start of the last token, or into the
+    // tree-masked new tokens (a real branch: most steps lie inside)
     if (!live || step_base + TILE > it.kv_end || step_base + TILE - 1 > it.causal_limit ||
-        step_base < it.window_lo + it.qo_count) {
+        step_base < it.window_lo + it.qo_count || (VAR && step_base + TILE > it.tree_lo)) {
       asm volatile("");
+      const bool tree = VAR && it.tree_lo != kNoTree;
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
-        const int tau = step_base + i * NG + grp;
-        const bool in_chunk = live && tau < it.kv_end;
+      for (int r = 0; r < ROWS; ++r) {
+        // the tree-mask row of this row's token (read on masked steps only)
+        const uint64_t trow = tree ? load_invariant(var.tree + it.qo_begin + r / g) : ~uint64_t(0);
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          const bool visible = in_chunk && tau <= it.causal_limit + r / g && tau >= it.window_lo + r / g;
+        for (int i = 0; i < TB; ++i) {
+          const int tau = step_base + i * NG + grp;
+          const bool in_chunk = live && tau < it.kv_end;
+          const bool in_tree = tau < it.tree_lo || ((trow >> ((tau - it.tree_lo) & 63)) & 1) != 0;
+          const bool visible =
+              in_chunk && tau <= it.causal_limit + r / g && tau >= it.window_lo + r / g && in_tree;
           s[i][r] = visible ? s[i][r] : kNegInf;
         }
       }
@@ -313,7 +334,7 @@ struct DecodeBody {
   // Attention of one work item; result in the workgroup-combined (O, log2-sum-exp)
   // handed to `emit(row, d_pair, o0, o1, lse2)`.
   template <typename Emit>
-  static __device__ void run(const RunParams& p, const WorkItem& it, float* lds, Emit&& emit) {
+  static __device__ void run(const RunParams& p, const WorkItem& it, const Variant& var, float* lds, Emit&& emit) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps loops scalar
     const int c = lane % LPT;
@@ -390,15 +411,15 @@ struct DecodeBody {
       while (true) {
         load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p0);
         load_kv(krs, vrs, c, p2, k2);
-        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k0, st);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k0, var, st);
         if (++j >= nt_w) break;
         load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p1);
         load_kv(krs, vrs, c, p0, k0);
-        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k1, st);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k1, var, st);
         if (++j >= nt_w) break;
         load_pids(p, irs, it, t0 + (j + 3) * kWaves, grp, p2);
         load_kv(krs, vrs, c, p1, k1);
-        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k2, st);
+        step(p, it, t0 + j * kWaves, grp, j >= 0, q, k2, var, st);
         if (++j >= nt_w) break;
       }
     }

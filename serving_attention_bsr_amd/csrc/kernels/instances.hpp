@@ -25,22 +25,23 @@ constexpr int kDecodeOcc = (BF16 && ROWS == 4) ? BSR_DECODE_OCC : 1;
 // workgroup per CU only shortens chunks (more partial states) and shares the CU.
 constexpr int kDecodeWgPerCu = 1;
 
-template <int D, bool BF16, int ROWS, bool CAP>
+template <int D, bool BF16, int ROWS, bool CAP, bool VAR>
 inline void add_decode(std::vector<KernelEntry>* out) {
-  out->push_back({KernelKey{kKindDecode, BF16, D, ROWS, CAP},
+  out->push_back({KernelKey{kKindDecode, BF16, D, ROWS, CAP, false, false, VAR},
                   reinterpret_cast<const void*>(
                       &bsr_persistent_kernel<D, BF16, ROWS, kDecodeTb<BF16>, CAP, kKindDecode,
-                                             kDecodeOcc<D, BF16, ROWS>>),
+                                             kDecodeOcc<D, BF16, ROWS>, false, false, VAR>),
                   kDecodeWgPerCu});
 }
 
 // FP8 (E4M3) K/V with bf16 Q/O: four KV rows per lane group and step, the bytes in
 // flight of the bf16 body's two.
-template <int D, int ROWS, bool CAP>
+template <int D, int ROWS, bool CAP, bool VAR>
 inline void add_decode_kv8(std::vector<KernelEntry>* out) {
-  out->push_back({KernelKey{kKindDecode, true, D, ROWS, CAP, false, true},
+  out->push_back({KernelKey{kKindDecode, true, D, ROWS, CAP, false, true, VAR},
                   reinterpret_cast<const void*>(
-                      &bsr_persistent_kernel<D, true, ROWS, 2 * kDecodeTb<true>, CAP, kKindDecode, 1, false, true>),
+                      &bsr_persistent_kernel<D, true, ROWS, 2 * kDecodeTb<true>, CAP, kKindDecode, 1, false, true,
+                                             VAR>),
                   kDecodeWgPerCu});
 }
 
@@ -50,45 +51,48 @@ inline void add_decode_kv8(std::vector<KernelEntry>* out) {
 template <int D>
 constexpr int kMfmaOcc = 2;
 
-template <int D, bool CAP, bool PAGE1>
+template <int D, bool CAP, bool PAGE1, bool VAR>
 inline void add_mfma(std::vector<KernelEntry>* out) {
-  out->push_back({KernelKey{kKindMfma, true, D, 0, CAP, PAGE1},
+  out->push_back({KernelKey{kKindMfma, true, D, 0, CAP, PAGE1, false, VAR},
                   reinterpret_cast<const void*>(
-                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, kMfmaOcc<D>, PAGE1>),
+                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, kMfmaOcc<D>, PAGE1, false,
+                                             VAR>),
                   kMfmaOcc<D>});
 }
 
-template <int D, int ROWS, bool CAP>
+template <int D, int ROWS, bool CAP, bool VAR>
 inline void add_mixed(std::vector<KernelEntry>* out) {
-  out->push_back({KernelKey{kKindMixed, true, D, ROWS, CAP},
+  out->push_back({KernelKey{kKindMixed, true, D, ROWS, CAP, false, false, VAR},
                   reinterpret_cast<const void*>(
-                      &bsr_persistent_kernel<D, true, ROWS, kDecodeTb<true>, CAP, kKindMixed, 1>),
+                      &bsr_persistent_kernel<D, true, ROWS, kDecodeTb<true>, CAP, kKindMixed, 1, false, false, VAR>),
                   1});
 }
 
-template <int D>
+// VAR: instances for plans with ALiBi slopes or tree masks (compiled in their own
+// translation units).
+template <int D, bool VAR>
 inline void register_head_dim(std::vector<KernelEntry>* out) {
-  add_mfma<D, false, false>(out);
-  add_mfma<D, true, false>(out);
+  add_mfma<D, false, false, VAR>(out);
+  add_mfma<D, true, false, VAR>(out);
   // one key per page (radix-tree layout): prefill without the page division
-  add_mfma<D, false, true>(out);
-  add_mfma<D, true, true>(out);
-  add_mixed<D, 4, false>(out);
-  add_mixed<D, 4, true>(out);
-  add_mixed<D, 8, false>(out);
-  add_mixed<D, 8, true>(out);
-  add_decode<D, true, 4, false>(out);
-  add_decode<D, true, 4, true>(out);
-  add_decode<D, true, 8, false>(out);
-  add_decode<D, true, 8, true>(out);
-  add_decode<D, false, 4, false>(out);
-  add_decode<D, false, 4, true>(out);
-  add_decode<D, false, 8, false>(out);
-  add_decode<D, false, 8, true>(out);
-  add_decode_kv8<D, 4, false>(out);
-  add_decode_kv8<D, 4, true>(out);
-  add_decode_kv8<D, 8, false>(out);
-  add_decode_kv8<D, 8, true>(out);
+  add_mfma<D, false, true, VAR>(out);
+  add_mfma<D, true, true, VAR>(out);
+  add_mixed<D, 4, false, VAR>(out);
+  add_mixed<D, 4, true, VAR>(out);
+  add_mixed<D, 8, false, VAR>(out);
+  add_mixed<D, 8, true, VAR>(out);
+  add_decode<D, true, 4, false, VAR>(out);
+  add_decode<D, true, 4, true, VAR>(out);
+  add_decode<D, true, 8, false, VAR>(out);
+  add_decode<D, true, 8, true, VAR>(out);
+  add_decode<D, false, 4, false, VAR>(out);
+  add_decode<D, false, 4, true, VAR>(out);
+  add_decode<D, false, 8, false, VAR>(out);
+  add_decode<D, false, 8, true, VAR>(out);
+  add_decode_kv8<D, 4, false, VAR>(out);
+  add_decode_kv8<D, 4, true, VAR>(out);
+  add_decode_kv8<D, 8, false, VAR>(out);
+  add_decode_kv8<D, 8, true, VAR>(out);
 }
 
 }  // namespace bsr

@@ -37,30 +37,30 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // KIND selects the attention bodies: decode only, MFMA only (bf16), or both
 // (chosen per work item).
-template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, bool PAGE1, bool KV8>
+template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, bool PAGE1, bool KV8, bool VAR>
 struct PersistentKernel {
   static_assert(KIND == kKindDecode || BF16, "the MFMA body is bf16 only");
   static_assert(KIND == kKindDecode || !KV8, "an FP8 K/V cache runs on the decode body only");
-  using Decode = DecodeBody<D, BF16, ROWS, TB, CAP, KV8>;
+  using Decode = DecodeBody<D, BF16, ROWS, TB, CAP, KV8, VAR>;
   // 32 rows per wavefront up to D = 128; 16 rows (two workgroups per CU) at D = 256
-  using Mfma = typename std::conditional<D == 256, MfmaBody16<D, CAP, PAGE1>, MfmaBody<D, CAP, PAGE1>>::type;
+  using Mfma = typename std::conditional<D == 256, MfmaBody16<D, CAP, PAGE1, VAR>, MfmaBody<D, CAP, PAGE1, VAR>>::type;
   using Merge = MergeBody<D, BF16>;
   static constexpr int LDS_FLOATS =
       cmax(Merge::LDS_FLOATS, cmax(KIND == kKindMfma ? 0 : Decode::LDS_FLOATS,
                                    KIND == kKindDecode ? 0 : Mfma::LDS_FLOATS));
 
   template <typename Emit>
-  static __device__ __forceinline__ void attend(const RunParams& p, const WorkItem& it, float* lds,
-                                                Emit&& emit) {
+  static __device__ __forceinline__ void attend(const RunParams& p, const WorkItem& it, const Variant& var,
+                                                float* lds, Emit&& emit) {
     if constexpr (KIND == kKindDecode) {
-      Decode::run(p, it, lds, emit);
+      Decode::run(p, it, var, lds, emit);
     } else if constexpr (KIND == kKindMfma) {
-      Mfma::run(p, it, lds, emit);
+      Mfma::run(p, it, var, lds, emit);
     } else {
       if (it.flags & kItemMfma)
-        Mfma::run(p, it, lds, emit);
+        Mfma::run(p, it, var, lds, emit);
       else
-        Decode::run(p, it, lds, emit);
+        Decode::run(p, it, var, lds, emit);
     }
   }
 };
@@ -81,16 +81,20 @@ struct PersistentKernel {
 
 // OCC: workgroups per CU the register allocation must allow.  PAGE1: the pool has
 // one key per page (MFMA bodies skip the page division).  KV8: K and V are FP8
-// E4M3 codes (decode body; Q and O bf16).
-template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, int OCC, bool PAGE1 = false, bool KV8 = false>
+// E4M3 codes (decode body; Q and O bf16).  VAR: plans with ALiBi slopes or tree
+// masks.
+template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, int OCC, bool PAGE1 = false, bool KV8 = false,
+          bool VAR = false>
 __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunParams p) {
-  using K = PersistentKernel<D, BF16, ROWS, TB, CAP, KIND, PAGE1, KV8>;
+  using K = PersistentKernel<D, BF16, ROWS, TB, CAP, KIND, PAGE1, KV8, VAR>;
   __shared__ float lds[K::LDS_FLOATS];
   uint8_t* ws = p.ws;
   // the whole header in one read (its fields are uniform; the empty asm keeps the
   // offsets from being loaded separately after the check below)
   const PlanHeader h = *plan_header(ws);
   asm volatile("" ::"s"(h.off_epochs), "s"(h.off_item_ptr), "s"(h.off_items), "s"(h.off_flags));
+  const Variant var{h.off_alibi != 0, reinterpret_cast<const float*>(ws + h.off_alibi),
+                    reinterpret_cast<const uint64_t*>(ws + h.off_tree)};
   const PlanHeader* hdr = &h;
   const int wg = blockIdx.x;
   int32_t* status = plan_i32(ws, hdr->off_status);
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   // another grid is refused as a whole: nothing is written but the status word,
   // which the host's check reports.  This is what a captured launch meets when a
   // later plan needs a different instance.
-  constexpr int32_t kKey = instance_key(KIND, KIND == kKindMfma ? 0 : ROWS, D, BF16, CAP, PAGE1, KV8);
+  constexpr int32_t kKey = instance_key(KIND, KIND == kKindMfma ? 0 : ROWS, D, BF16, CAP, PAGE1, KV8, VAR);
   if (hdr->instance != kKey || hdr->num_wg != static_cast<int32_t>(gridDim.x)) {
     if (wg == 0 && threadIdx.x == 0) status[kStatusWrongKernel] = 1;
     return;
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
           __hip_atomic_store(reinterpret_cast<uint32_t*>(pl + row), __float_as_uint(lse2), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
       };
-      K::attend(p, it, lds, emit);
+      K::attend(p, it, var, lds, emit);
       any_partial = true;
     } else {
       auto emit = [&](int r, int d, float o0, float o1, float lse2) {
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
         }
         if (d == 0 && p.lse != nullptr) p.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
       };
-      K::attend(p, it, lds, emit);
+      K::attend(p, it, var, lds, emit);
     }
   }
 

@@ -41,7 +41,8 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 // PAGE1: every page holds one key (page size 1, the radix-tree layout), so a key's
 // page is its own position and no division is needed.
-template <int D, bool CAP, bool PAGE1 = false>
+// VAR: the plan may carry ALiBi slopes and tree masks.
+template <int D, bool CAP, bool PAGE1 = false, bool VAR = false>
 struct MfmaBody {
   static constexpr int BR = 128;           // folded rows per item
   static constexpr int BC = 64;            // keys per tile
@@ -147,28 +148,46 @@ struct MfmaBody {
     }
   }
 
-  // Soft-cap (base 2) and the chunk-end / causal mask of tile t.
+  // ALiBi bias, soft-cap (base 2) and the chunk-end / causal / window / tree mask
+  // of tile t.  slope and pos are this lane's row's ALiBi slope (unscaled-logit
+  // units) and query position, tm its token's tree-mask row.
   static __device__ __forceinline__ void cap_and_mask(const RunParams& p, const WorkItem& it, int t, int t_local,
-                                                      int half, f32x16_t (&s)[KB]) {
+                                                      int half, bool alibi, float slope, int pos, uint64_t tm,
+                                                      f32x16_t (&s)[KB]) {
+    const int tile_base = it.kv_begin + t * BC;
+    if (VAR && alibi) {
+      // key 32 kb + 8 (r / 4) + 4 half + r % 4 of the tile gains slope (key - pos)
+      const float base = static_cast<float>(tile_base + 4 * half - pos);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = __builtin_fmaf(slope, base + static_cast<float>(32 * kb + 8 * (r >> 2) + (r & 3)), s[kb][r]);
+    }
     if constexpr (CAP) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = p.cap_log2 * tanh_exp(s[kb][r] * p.sm_scale * p.cap_inv);
     }
-    const int tile_base = it.kv_begin + t * BC;
-    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit || tile_base < it.window_lo + it.qo_count) {
+    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit || tile_base < it.window_lo + it.qo_count ||
+        (VAR && tile_base + BC > it.tree_lo)) {
       // key 32 kb + 8 (r / 4) + 4 half + r % 4 of the tile is visible up to the
       // chunk end and this row's causal limit
       asm volatile("");  // keep this a branch: only boundary tiles pay for the mask
       const int lim = min(it.kv_end - 1, it.causal_limit + t_local) - tile_base - 4 * half;
       // and from this row's sliding-window start on
       const int low = max(it.window_lo + t_local, it.kv_begin) - tile_base - 4 * half;
+      // and, among the tree-masked new tokens, where the token's tree row allows
+      const int tlo = VAR ? it.tree_lo - tile_base - 4 * half : kNoTree;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim || 32 * kb + 8 * (r >> 2) + (r & 3) < low) s[kb][r] = kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          const int kr = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const bool tree_hides = kr >= tlo && ((tm >> ((kr - tlo) & 63)) & 1) == 0;
+          if (kr > lim || kr < low || tree_hides) s[kb][r] = kNegInf;
+        }
     }
   }
 
@@ -242,7 +261,8 @@ struct MfmaBody {
   }
 
   template <typename Emit>
-  static __device__ void run(const RunParams& p, const WorkItem& it, float* lds_f, Emit&& emit) {
+  static __device__ void run(const RunParams& p, const WorkItem& it, const Variant& var, float* lds_f,
+                             Emit&& emit) {
     uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_f);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -255,6 +275,12 @@ struct MfmaBody {
     const int t_local = rho / g;
     const int key_off = 4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2);
     const int d_off = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // variant state of this lane's row: ALiBi slope and position, tree-mask row
+    const bool alibi = VAR && var.has_alibi;
+    const float slope = alibi && row_ok ? var.alibi[it.kv_head * g + rho % g] : 0.0f;
+    const int pos = it.q_pos + t_local;
+    const uint64_t tm =
+        VAR && it.tree_lo != kNoTree && row_ok ? var.tree[it.qo_begin + t_local] : ~uint64_t(0);
 
     // Q rows of this wavefront as the B operand: Q[rho][16 ks + 8 half + 0..7]
     bf16x8_t qreg[DK];
@@ -317,7 +343,7 @@ struct MfmaBody {
         if (more) gather(krs, vrs, rpp, rows, nb, wave, lane, h * NI / H, (h + 1) * NI / H);
       });
       if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);
-      cap_and_mask(p, it, t, t_local, half, s);
+      cap_and_mask(p, it, t, t_local, half, alibi, slope, pos, tm, s);
       bf16x8_t pb[KB][2];
       const float alpha = softmax(s, c, m_run, l_run, pb);
       rescale(alpha, acc);

@@ -35,7 +35,8 @@ namespace bsr {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // PAGE1: every page holds one key, so a key's page is its own position.
-template <int D, bool CAP, bool PAGE1 = false>
+// VAR: the plan may carry ALiBi slopes and tree masks.
+template <int D, bool CAP, bool PAGE1 = false, bool VAR = false>
 struct MfmaBody16 {
   static constexpr int BR = 64;            // folded rows per item
   static constexpr int BC = 32;            // keys per tile
@@ -130,28 +131,44 @@ struct MfmaBody16 {
     }
   }
 
-  // Soft-cap (base 2) and the chunk-end / causal mask of tile t.
+  // ALiBi bias, soft-cap (base 2) and the chunk-end / causal / window / tree mask
+  // of tile t (see MfmaBody::cap_and_mask).
   static __device__ __forceinline__ void cap_and_mask(const RunParams& p, const WorkItem& it, int t, int t_local,
-                                                      int grp, f32x4_t (&s)[KB]) {
+                                                      int grp, bool alibi, float slope, int pos, uint64_t tm,
+                                                      f32x4_t (&s)[KB]) {
+    const int tile_base = it.kv_begin + t * BC;
+    if (VAR && alibi) {
+      // key 16 kb + 4 grp + i of the tile gains slope (key - pos)
+      const float base = static_cast<float>(tile_base + 4 * grp - pos);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kb][i] = __builtin_fmaf(slope, base + static_cast<float>(16 * kb + i), s[kb][i]);
+    }
     if constexpr (CAP) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[kb][i] = p.cap_log2 * tanh_exp(s[kb][i] * p.sm_scale * p.cap_inv);
     }
-    const int tile_base = it.kv_begin + t * BC;
-    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit || tile_base < it.window_lo + it.qo_count) {
+    if (tile_base + BC > it.kv_end || tile_base + BC - 1 > it.causal_limit || tile_base < it.window_lo + it.qo_count ||
+        (VAR && tile_base + BC > it.tree_lo)) {
       asm volatile("");  // keep this a branch: only boundary tiles pay for the mask
       // key 16 kb + 4 grp + i of the tile is visible up to the chunk end and this
       // row's causal limit
       const int lim = min(it.kv_end - 1, it.causal_limit + t_local) - tile_base - 4 * grp;
       // and from this row's sliding-window start on
       const int low = max(it.window_lo + t_local, it.kv_begin) - tile_base - 4 * grp;
+      // and, among the tree-masked new tokens, where the token's tree row allows
+      const int tlo = VAR ? it.tree_lo - tile_base - 4 * grp : kNoTree;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * kb + i > lim || 16 * kb + i < low) s[kb][i] = kNegInf;
+        for (int i = 0; i < 4; ++i) {
+          const int kr = 16 * kb + i;
+          const bool tree_hides = kr >= tlo && ((tm >> ((kr - tlo) & 63)) & 1) == 0;
+          if (kr > lim || kr < low || tree_hides) s[kb][i] = kNegInf;
+        }
     }
   }
 
@@ -214,7 +231,8 @@ struct MfmaBody16 {
   }
 
   template <typename Emit>
-  static __device__ void run(const RunParams& p, const WorkItem& it, float* lds_f, Emit&& emit) {
+  static __device__ void run(const RunParams& p, const WorkItem& it, const Variant& var, float* lds_f,
+                             Emit&& emit) {
     uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_f);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -227,6 +245,12 @@ struct MfmaBody16 {
     const int t_local = rho / g;
     const int key_off = 4 * grp + (r16 >> 2);
     const int d_off = 4 * (r16 & 3);
+    // variant state of this lane's row: ALiBi slope and position, tree-mask row
+    const bool alibi = VAR && var.has_alibi;
+    const float slope = alibi && row_ok ? var.alibi[it.kv_head * g + rho % g] : 0.0f;
+    const int pos = it.q_pos + t_local;
+    const uint64_t tm =
+        VAR && it.tree_lo != kNoTree && row_ok ? var.tree[it.qo_begin + t_local] : ~uint64_t(0);
 
     // Q rows as the B operand: Q[rho][32 ks + 8 grp + 0..7]
     bf16x8_t qreg[DK];
@@ -274,7 +298,7 @@ struct MfmaBody16 {
         gather<NI / 2, NI>(krs, vrs, rpp, rows, nb, wave, lane);
         if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);
       }
-      cap_and_mask(p, it, t, t_local, grp, s);
+      cap_and_mask(p, it, t, t_local, grp, alibi, slope, pos, tm, s);
       bf16x8_t pb;
       const float alpha = softmax(s, c, m_run, l_run, pb);
       rescale(alpha, acc);

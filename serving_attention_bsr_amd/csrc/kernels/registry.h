@@ -17,5 +17,9 @@ struct KernelEntry {
 void register_d64(std::vector<KernelEntry>* out);
 void register_d128(std::vector<KernelEntry>* out);
 void register_d256(std::vector<KernelEntry>* out);
+// instances for plans with ALiBi slopes or tree masks
+void register_d64_var(std::vector<KernelEntry>* out);
+void register_d128_var(std::vector<KernelEntry>* out);
+void register_d256_var(std::vector<KernelEntry>* out);
 
 }  // namespace bsr

@@ -2,5 +2,5 @@
 #include "kernels/instances.hpp"
 
 namespace bsr {
-void register_d256(std::vector<KernelEntry>* out) { register_head_dim<256>(out); }
+void register_d256(std::vector<KernelEntry>* out) { register_head_dim<256, false>(out); }
 }  // namespace bsr

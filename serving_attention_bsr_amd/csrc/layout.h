@@ -24,6 +24,9 @@
 //   merge_ptr[num_wg + 1]  merge tasks of workgroup w
 //   merge[num_merge]       MergeTask
 //   srcs[num_srcs]         MergeSrc, grouped per task
+//   alibi[H_qo]            (ALiBi plans) slope / sm_scale of each query head
+//   tree[total_qo]         (tree-masked plans) uint64 per query token: bit u set iff
+//                          the token sees its block row's key tree_lo + u
 #pragma once
 
 #include <stdint.h>
@@ -35,6 +38,8 @@ constexpr int kWgThreads = 256;             // 4 wavefronts of 64
 constexpr int kWaves = 4;
 constexpr int32_t kNoCausal = 0x3fffffff;   // causal_limit meaning "every key visible"
 constexpr int32_t kNoWindow = -0x3fffffff;  // window_lo meaning "no lower bound"
+constexpr int32_t kNoTree = 0x3fffffff;     // tree_lo meaning "no tree mask"
+constexpr int kMaxTreeTokens = 64;          // new tokens of a tree-masked request (one 64-bit row each)
 
 enum KernelKind : int32_t { kKindDecode = 1, kKindMfma = 2, kKindMixed = 3 };
 
@@ -49,21 +54,23 @@ enum StatusWord : int32_t {
 };
 
 // Identity of the persistent-kernel instance a plan is made for: the kernel kind,
-// the decode body's folded rows (0 for the MFMA-only kind), the head dim, and the
-// handle-level switches that select an instance.  The planner writes it into the
+// the decode body's folded rows (0 for the MFMA-only kind), the head dim, the
+// handle-level switches that select an instance, and whether the plan carries
+// variant data (ALiBi slopes, tree masks).  The planner writes it into the
 // header and the kernel compares it with its own template arguments, so a launch
 // captured for one instance never runs a later plan made for another (for
 // example a decode graph captured at 4 folded rows replaying an 8-row plan).
-constexpr int32_t instance_key(int kind, int rows, int head_dim, bool bf16, bool cap, bool page1, bool kv8) {
+constexpr int32_t instance_key(int kind, int rows, int head_dim, bool bf16, bool cap, bool page1, bool kv8,
+                               bool var) {
   return kind | (rows << 4) | ((head_dim / 64) << 8) | (bf16 ? 1 << 12 : 0) | (cap ? 1 << 13 : 0) |
-         (page1 ? 1 << 14 : 0) | (kv8 ? 1 << 15 : 0);
+         (page1 ? 1 << 14 : 0) | (kv8 ? 1 << 15 : 0) | (var ? 1 << 16 : 0);
 }
 
 // Default bound of a merge's wait for one ready stamp, in polls (each poll sleeps
 // briefly); the planner writes it into the header.
 constexpr int32_t kDefaultSpinLimit = 1 << 21;
 
-struct WorkItem {  // 48 bytes
+struct WorkItem {  // 64 bytes
   int32_t flags;
   int32_t qo_begin;      // first query token (row of Q/O) of the tile
   int32_t qo_count;      // query tokens in the tile (folded rows = qo_count * g)
@@ -75,7 +82,9 @@ struct WorkItem {  // 48 bytes
   int32_t partial_row;   // first folded row of the partial state, or -1
   int32_t flag_id;       // ready-flag slot of the partial state, or -1
   int32_t window_lo;     // token i of the tile sees keys j >= window_lo + i
-  int32_t pad1;
+  int32_t q_pos;         // position of the tile's first token (l_kv - l_qo + t0; ALiBi)
+  int32_t tree_lo;       // first key of the block row's tree-masked new tokens, or kNoTree
+  int32_t pad[3];
 };
 
 struct MergeTask {  // 16 bytes: combine the states of g folded rows of one token
@@ -109,10 +118,11 @@ struct PlanHeader {  // 80 bytes
   int32_t blob_bytes;
   int32_t instance;    // instance_key() of the kernel this plan is made for
   int32_t spin_limit;  // polls before a merge gives up on a ready stamp
-  int32_t reserved[2];
+  int32_t off_alibi;   // float [H_qo] ALiBi slopes / sm_scale, or 0 without ALiBi
+  int32_t off_tree;    // uint64 [total_qo] tree-mask rows, or 0 without tree masks
 };
 
-static_assert(sizeof(WorkItem) == 48, "WorkItem layout");
+static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
 static_assert(sizeof(MergeTask) == 16, "MergeTask layout");
 static_assert(sizeof(MergeSrc) == 8, "MergeSrc layout");
 static_assert(sizeof(PlanHeader) == 80, "PlanHeader layout");

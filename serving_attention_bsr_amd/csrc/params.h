@@ -37,6 +37,7 @@ struct KernelKey {
   bool cap;
   bool page1 = false;  // instance specialised for one key per page (MFMA kind only)
   bool kv8 = false;    // K/V are FP8 E4M3 codes, Q/O bf16 (decode kind only)
+  bool var = false;    // plans with ALiBi slopes or tree masks
 };
 
 // Host stub of the matching persistent kernel, or null if not built; the

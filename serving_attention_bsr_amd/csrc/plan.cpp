@@ -58,6 +58,8 @@ struct Unit {
   int32_t l_eff;  // keys the unit reads: kv_lo .. kv_lo + l_eff - 1
   int32_t causal_limit;
   int32_t window_lo;
+  int32_t q_pos;    // position of the unit's first token (l_kv - l_qo + t0)
+  int32_t tree_lo;  // first key of the row's tree-masked tokens, or kNoTree
   bool mfma;
   int32_t w16;  // cost of one KV token in sixteenths (16 except MFMA units of a mixed grid)
 };
@@ -167,6 +169,8 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
     w.page_begin = r.page_begin;
     w.causal_limit = u.causal_limit;
     w.window_lo = u.window_lo;
+    w.q_pos = u.q_pos;
+    w.tree_lo = u.tree_lo;
     w.partial_row = -1;
     w.flag_id = -1;
     return w;
@@ -449,7 +453,7 @@ static void assign_merges(const PlanConfig& cfg, int32_t nwg, const std::vector<
 }
 
 int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t total_qo,
-              bool composable, PlanResult* out, std::string* err) {
+              bool composable, PlanResult* out, std::string* err, const std::vector<uint64_t>* tree_rows) {
   const int32_t g = cfg.group;
   const int32_t h_kv = cfg.h_kv;
 
@@ -494,7 +498,8 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       q_tile = tile;
     }
   }
-  const int32_t nwg = cfg.num_wg[kernel][kernel != kKindMfma && decode_rows == 8 ? 1 : 0];
+  const bool var = !cfg.alibi_raw.empty() || tree_rows != nullptr;
+  const int32_t nwg = cfg.num_wg[kernel][kernel != kKindMfma && decode_rows == 8 ? 1 : 0][var ? 1 : 0];
   if (nwg <= 0) {
     *err = "the kernel this plan needs (kind " + std::to_string(kernel) + ") is not built for this handle";
     return BSR_ERR_UNSUPPORTED;
@@ -539,6 +544,8 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
           u.causal_limit = kNoCausal;
           end = r.kv_len;
         }
+        u.q_pos = r.kv_len - r.qo_len + t0;
+        u.tree_lo = r.tree ? r.kv_len - r.qo_len : kNoTree;
         // a sliding window hides keys below window_lo + t from token t: the unit
         // starts at its first token's window, rounded down to the chunk granule so
         // chunk starts stay where the bodies expect them
@@ -628,7 +635,7 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   hdr.num_srcs = static_cast<int32_t>(srcs.size());
   hdr.num_flags = num_flags;
   hdr.instance = instance_key(kernel, kernel == kKindMfma ? 0 : decode_rows, cfg.head_dim, cfg.bf16, cfg.cap,
-                              kernel == kKindMfma && cfg.page_size == 1, cfg.kv8);
+                              kernel == kKindMfma && cfg.page_size == 1, cfg.kv8, var);
   hdr.spin_limit = kDefaultSpinLimit;
   int64_t off = sizeof(PlanHeader);
   hdr.off_status = align16(off);
@@ -647,6 +654,14 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   off = hdr.off_merge + static_cast<int64_t>(sizeof(MergeTask)) * tasks.size();
   hdr.off_srcs = align16(off);
   off = hdr.off_srcs + static_cast<int64_t>(sizeof(MergeSrc)) * srcs.size();
+  if (!cfg.alibi_raw.empty()) {
+    hdr.off_alibi = align16(off);
+    off = hdr.off_alibi + 4LL * static_cast<int64_t>(cfg.alibi_raw.size());
+  }
+  if (tree_rows != nullptr) {
+    hdr.off_tree = align16(off);
+    off = hdr.off_tree + 8LL * total_qo;
+  }
   const int64_t bytes = align16(off);
   if (bytes > cfg.blob_capacity) {
     *err = "plan of " + std::to_string(bytes) + " bytes exceeds the plan segment (" +
@@ -678,9 +693,14 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
     for (int32_t i : morder) dst[fill[mowner[i]]++] = tasks[i];
     if (!srcs.empty()) std::memcpy(base + hdr.off_srcs, srcs.data(), sizeof(MergeSrc) * srcs.size());
   }
+  if (hdr.off_alibi != 0)
+    std::memcpy(base + hdr.off_alibi, cfg.alibi_raw.data(), 4 * cfg.alibi_raw.size());
+  if (hdr.off_tree != 0 && total_qo > 0)
+    std::memcpy(base + hdr.off_tree, tree_rows->data(), 8LL * total_qo);
 
   out->kernel = kernel;
   out->num_wg = nwg;
+  out->var = var;
   out->q_tile = q_tile;
   out->decode_rows = decode_rows;
   out->num_items = hdr.num_items;

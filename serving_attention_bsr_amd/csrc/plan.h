@@ -20,8 +20,8 @@ struct PlanConfig {
   bool causal = false;
   bool bf16 = false;
   bool cap = false;  // logits soft-cap on (selects the kernel instance)
-  // grid per kernel instance: [KernelKind][decode rows 4 -> 0, 8 -> 1]
-  int32_t num_wg[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+  // grid per kernel instance: [KernelKind][decode rows 4 -> 0, 8 -> 1][variant data]
+  int32_t num_wg[4][2][2] = {};
   int64_t alpha = 1, beta = 1;
   int64_t gamma = 512;       // fixed cost of a work item or merge task (KV-token units)
   int32_t min_chunk = 64;
@@ -34,6 +34,8 @@ struct PlanConfig {
   bool kv8 = false;  // K/V are FP8 codes: decode body only (no MFMA tiles)
   int32_t slot2_speed16 = 16;
   int32_t window = 0;  // sliding window in keys (0: none)
+  // ALiBi: per query head, slope / sm_scale (empty: no ALiBi)
+  std::vector<float> alibi_raw;
   // capacities (plan rejected beyond them)
   int32_t max_batch = 0, max_total_qo = 0;
   int64_t max_total_kv = 0;
@@ -47,11 +49,13 @@ struct BlockRow {
   int32_t page_begin = 0;  // absolute index into kv_indices
   int32_t kv_len = 0;
   int32_t format = 0;
+  bool tree = false;  // the row's new tokens carry tree-mask rows
 };
 
 struct PlanResult {
   std::vector<uint8_t> blob;  // the bytes to upload
   int32_t kernel = 0, num_wg = 0, q_tile = 0, decode_rows = 0;
+  bool var = false;  // the plan carries variant data (ALiBi slopes, tree masks)
   int32_t num_items = 0, num_partial_items = 0, num_merge = 0, num_srcs = 0;
   int64_t num_partial_rows = 0;
   int64_t kv_chunk = 0, max_wg_cost = 0, total_cost = 0;
@@ -69,7 +73,10 @@ constexpr int kChunkCandidates = 4;
 inline int32_t mfma_tile(int32_t head_dim) { return head_dim == 256 ? 64 : 128; }
 
 // Returns 0 and fills out, or a bsr_status code with a message in err.
+// tree_rows: null, or one 64-bit tree-mask row per query token (rows of block
+// rows whose `tree` is set; bit u: the token sees key l_kv - l_qo + u).
 int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t total_qo,
-              bool composable, PlanResult* out, std::string* err);
+              bool composable, PlanResult* out, std::string* err,
+              const std::vector<uint64_t>* tree_rows = nullptr);
 
 }  // namespace bsr

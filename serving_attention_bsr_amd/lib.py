@@ -38,6 +38,7 @@ EXPORTED = [
     "bsr_attn_create",
     "bsr_attn_workspace_size",
     "bsr_attn_plan",
+    "bsr_attn_plan_tree_mask",
     "bsr_attn_plan_composable",
     "bsr_attn_plan_get_info",
     "bsr_attn_run",
@@ -78,6 +79,7 @@ class bsr_attn_config(ctypes.Structure):
         ("slot2_speed", ctypes.c_int32),
         ("sliding_window", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+        ("alibi_slopes", ctypes.POINTER(ctypes.c_float)),
     ]
 
 
@@ -113,7 +115,7 @@ class bsr_plan_info(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 2  # BSR_ATTN_ABI_VERSION of the struct layouts above
+ABI_VERSION = 3  # BSR_ATTN_ABI_VERSION of the struct layouts above
 
 
 def load():
@@ -132,6 +134,7 @@ def load():
     lib.bsr_attn_create.argtypes = [ctypes.POINTER(bsr_attn_config), c_int, ctypes.POINTER(vp)]
     lib.bsr_attn_workspace_size.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     lib.bsr_attn_plan.argtypes = [vp, i32p, i32p, i32p, c_i32, vp, vp, vp]
+    lib.bsr_attn_plan_tree_mask.argtypes = [vp, i32p, i32p, i32p, c_i32, vp, vp, vp, vp]
     lib.bsr_attn_plan_composable.argtypes = [vp, c_i32, ctypes.POINTER(bsr_format), c_i32, vp, vp, vp]
     lib.bsr_attn_plan_get_info.argtypes = [vp, ctypes.POINTER(bsr_plan_info)]
     lib.bsr_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, f32p, vp, vp]
@@ -202,6 +205,24 @@ def bsr_attn_plan(h, qo_indptr, kv_indptr, last_page_len, workspace, host_stagin
     qo, kv, last = _i32(qo_indptr), _i32(kv_indptr), _i32(last_page_len)
     batch = len(qo) - 1
     _check(load().bsr_attn_plan(h, _ptr(qo), _ptr(kv), _ptr(last), batch, workspace, host_staging, stream))
+
+
+def bsr_attn_plan_tree_mask(h, qo_indptr, kv_indptr, last_page_len, tree_mask_bits, workspace, host_staging,
+                            stream):
+    """tree_mask_bits: uint8 array, the packed bits described in the header."""
+    qo, kv, last = _i32(qo_indptr), _i32(kv_indptr), _i32(last_page_len)
+    bits = np.ascontiguousarray(np.asarray(tree_mask_bits, dtype=np.uint8))
+    batch = len(qo) - 1
+    _check(load().bsr_attn_plan_tree_mask(h, _ptr(qo), _ptr(kv), _ptr(last), batch, ctypes.c_void_p(bits.ctypes.data),
+                                          workspace, host_staging, stream))
+
+
+def pack_tree_masks(masks):
+    """Pack per-request boolean [l_qo, l_qo] tree masks into the library's bit layout
+    (request after request, row-major, least significant bit first)."""
+    flat = [np.asarray(m, dtype=bool).reshape(-1) for m in masks]
+    bits = np.concatenate(flat) if flat else np.zeros(0, dtype=bool)
+    return np.packbits(bits, bitorder="little")
 
 
 def bsr_attn_plan_composable(h, formats: Sequence[dict], total_qo, workspace, host_staging, stream):
@@ -285,6 +306,7 @@ class BsrAttention:
         cost_mfma: int = 0,
         slot2_speed: int = 0,
         sliding_window: int = 0,
+        alibi_slopes=None,
     ):
         cfg = bsr_attn_config()
         cfg.num_qo_heads = num_qo_heads
@@ -307,10 +329,16 @@ class BsrAttention:
         cfg.cost_mfma = cost_mfma
         cfg.slot2_speed = slot2_speed
         cfg.sliding_window = sliding_window
+        if alibi_slopes is not None:
+            slopes = np.ascontiguousarray(np.asarray(alibi_slopes, dtype=np.float32))
+            if slopes.shape != (num_qo_heads,):
+                raise ValueError("alibi_slopes must hold one slope per query head")
+            cfg.alibi_slopes = slopes.ctypes.data_as(ctypes.POINTER(ctypes.c_float))  # read by create only
         self.cfg = cfg
         self.dtype = dtype
         self.device = device
         self.handle = bsr_attn_create(cfg, device)
+        cfg.alibi_slopes = None
         dev_bytes, host_bytes = bsr_attn_workspace_size(self.handle)
         self.workspace_bytes = dev_bytes
         if device >= 0:
@@ -338,6 +366,13 @@ class BsrAttention:
         run_static, which uploads it into the library's static scratch)."""
         ws = self._ws_ptr if upload else None
         bsr_attn_plan(self.handle, qo_indptr, kv_indptr, last_page_len, ws, self._staging_ptr, self._stream())
+        return self.info()
+
+    def plan_tree_mask(self, qo_indptr, kv_indptr, last_page_len, masks, upload=True):
+        """Plan with a tree mask per request (boolean [l_qo, l_qo] each)."""
+        ws = self._ws_ptr if upload else None
+        bsr_attn_plan_tree_mask(self.handle, qo_indptr, kv_indptr, last_page_len, pack_tree_masks(masks), ws,
+                                self._staging_ptr, self._stream())
         return self.info()
 
     def plan_composable(self, formats, total_qo):

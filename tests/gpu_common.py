@@ -63,7 +63,7 @@ def run_gpu(w, h=None, composable=False, **kw):
     return o.double().cpu().numpy(), lse.double().cpu().numpy(), info
 
 
-def oracle_of(w, composable=False):
+def oracle_of(w, composable=False, alibi_slopes=None, tree_masks=None):
     q = w.q.double().numpy()
     if w.k_pool.dtype == torch.float8_e4m3fn:
         # the oracle decodes the E4M3 codes itself
@@ -80,6 +80,7 @@ def oracle_of(w, composable=False):
     return oracle.bsr_attention(
         q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, w.page_size,
         w.num_qo_heads, w.num_kv_heads, w.scale, w.causal, w.cap, w.window,
+        alibi_slopes=alibi_slopes, tree_masks=tree_masks,
     )
 
 

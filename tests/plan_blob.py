@@ -2,7 +2,7 @@
 
 The layout decoded here is the one documented in the library's layout header:
 an 80-byte header of int32 counts, offsets, the kernel instance and the wait bound, then status words, per-workgroup epochs,
-ready flags, per-workgroup item queues (CSR), 48-byte work items, per-workgroup
+ready flags, per-workgroup item queues (CSR), 64-byte work items, per-workgroup
 merge queues (CSR), 16-byte merge tasks and 8-byte merge sources.
 
 The executor runs the plan's work items and merge map with the oracle's
@@ -19,14 +19,16 @@ import oracle
 HEADER_FIELDS = [
     "magic", "kernel", "num_wg", "num_items", "num_merge", "num_srcs", "num_flags",
     "off_status", "off_epochs", "off_flags", "off_item_ptr", "off_items", "off_merge_ptr",
-    "off_merge", "off_srcs", "blob_bytes", "instance", "spin_limit", "reserved0", "reserved1",
+    "off_merge", "off_srcs", "blob_bytes", "instance", "spin_limit", "off_alibi", "off_tree",
 ]
 HEADER_BYTES = 4 * len(HEADER_FIELDS)
 ITEM = np.dtype([
     ("flags", "<i4"), ("qo_begin", "<i4"), ("qo_count", "<i4"), ("kv_head", "<i4"),
     ("page_begin", "<i4"), ("kv_begin", "<i4"), ("kv_end", "<i4"), ("causal_limit", "<i4"),
-    ("partial_row", "<i4"), ("flag_id", "<i4"), ("window_lo", "<i4"), ("pad1", "<i4"),
+    ("partial_row", "<i4"), ("flag_id", "<i4"), ("window_lo", "<i4"), ("q_pos", "<i4"), ("tree_lo", "<i4"),
+    ("pad0", "<i4"), ("pad1", "<i4"), ("pad2", "<i4"),
 ])
+NO_TREE = 0x3FFFFFFF
 TASK = np.dtype([("qo_row", "<i4"), ("kv_head", "<i4"), ("src_begin", "<i4"), ("src_count", "<i4")])
 SRC = np.dtype([("partial_row", "<i4"), ("flag_id", "<i4")])
 ITEM_MFMA = 1
@@ -43,7 +45,12 @@ def decode(blob: np.ndarray) -> dict:
     def arr(off, dtype, n):
         return np.frombuffer(blob[off : off + np.dtype(dtype).itemsize * n].tobytes(), dtype=dtype)
 
+    tree = None
+    if hdr["off_tree"]:
+        end = hdr["off_tree"] + 8 * ((hdr["blob_bytes"] - hdr["off_tree"]) // 8)
+        tree = np.frombuffer(blob[hdr["off_tree"] : end].tobytes(), dtype="<u8")
     return dict(
+        tree=tree,
         header=hdr,
         epochs=arr(hdr["off_epochs"], "<i4", nwg),
         flags=arr(hdr["off_flags"], "<i4", hdr["num_flags"]),
@@ -55,8 +62,11 @@ def decode(blob: np.ndarray) -> dict:
     )
 
 
-def execute(plan, q, k_pool, v_pool, kv_indices, group, page_size, scale, cap):
-    """Run the decoded plan on the CPU in float64; returns O, LSE (natural log)."""
+def execute(plan, q, k_pool, v_pool, kv_indices, group, page_size, scale, cap, alibi_slopes=None):
+    """Run the decoded plan on the CPU in float64; returns O, LSE (natural log).
+
+    Positions (ALiBi) and tree-mask rows come from the plan; the slopes are the
+    caller's (the plan holds them divided by the scale, in float32)."""
     total, h_qo, d = q.shape
     out = np.zeros((total, h_qo, v_pool.shape[3]))
     lse = np.full((total, h_qo), -np.inf)
@@ -74,10 +84,19 @@ def execute(plan, q, k_pool, v_pool, kv_indices, group, page_size, scale, cap):
                 token = int(it["qo_begin"]) + t
                 limit = int(it["causal_limit"]) + t
                 vis = (tau <= limit) & (tau >= int(it["window_lo"]) + t)
+                tlo = int(it["tree_lo"])
+                if tlo != NO_TREE:
+                    row = np.uint64(plan["tree"][token])
+                    bit = np.clip(tau - tlo, 0, 63).astype(np.uint64)
+                    vis &= (tau < tlo) | (((row >> bit) & np.uint64(1)) == 1)
                 for j in range(group):
                     head = int(it["kv_head"]) * group + j
+                    bias = None
+                    if alibi_slopes is not None:
+                        bias = (float(alibi_slopes[head]) * (tau[vis] - (int(it["q_pos"]) + t)))[None, :]
                     o1, l1 = oracle.attention_dense(
-                        np.asarray(q[token : token + 1, head, :], dtype=np.float64), k[vis], v[vis], scale, cap
+                        np.asarray(q[token : token + 1, head, :], dtype=np.float64), k[vis], v[vis], scale, cap,
+                        bias=bias,
                     )
                     if it["flags"] & ITEM_PARTIAL:
                         row = int(it["partial_row"]) + t * group + j

@@ -52,7 +52,12 @@ int main(int argc, char** argv) {
     cfg.causal = !composable && pick(0, 1) == 1;
     cfg.window = (!composable && pick(0, 3) == 0) ? pick(1, 3000) : 0;
     const int nwg = pick(1, 96);
-    for (int k = 0; k < 4; ++k) cfg.num_wg[k][0] = cfg.num_wg[k][1] = nwg;
+    for (int k = 0; k < 4; ++k)
+      for (int r = 0; r < 2; ++r) cfg.num_wg[k][r][0] = cfg.num_wg[k][r][1] = nwg;
+    if (!composable && pick(0, 3) == 0) {
+      cfg.alibi_raw.resize(cfg.h_qo);
+      for (float& a : cfg.alibi_raw) a = 0.01f * pick(-100, 100);
+    }
     cfg.cus = pick(0, 1) ? nwg / 2 : 0;
     cfg.slot2_speed16 = pick(8, 16);
     cfg.mfma_w16 = pick(16, 400);
@@ -103,9 +108,21 @@ int main(int argc, char** argv) {
         rows.push_back(s);
       }
     }
+    // tree masks on some single-format batches (rows of at most 64 tokens)
+    std::vector<uint64_t> tree;
+    bool use_tree = !composable && pick(0, 3) == 0;
+    for (const BlockRow& b : rows) use_tree = use_tree && b.qo_len <= kMaxTreeTokens && b.qo_len <= b.kv_len;
+    if (use_tree) {
+      tree.assign(total_qo, 0);
+      for (BlockRow& b : rows) {
+        b.tree = b.qo_len > 0;
+        for (int t = 0; t < b.qo_len; ++t)
+          tree[b.qo_begin + t] = (uint64_t(rng()) << 32 | rng()) | (uint64_t(1) << t);
+      }
+    }
     PlanResult res;
     std::string err;
-    const int rc = make_plan(cfg, rows, total_qo, composable, &res, &err);
+    const int rc = make_plan(cfg, rows, total_qo, composable, &res, &err, use_tree ? &tree : nullptr);
     CHECK(rc == BSR_OK || rc == BSR_ERR_UNSUPPORTED || rc == BSR_ERR_CAPACITY);
     if (rc != BSR_OK) continue;
     ++planned;
@@ -136,6 +153,7 @@ int main(int argc, char** argv) {
       CHECK(it.kv_begin >= 0 && it.kv_begin <= it.kv_end);
       CHECK(it.qo_count >= 1 && it.qo_begin >= 0 && it.qo_begin + it.qo_count <= total_qo);
       CHECK(it.kv_head >= 0 && it.kv_head < cfg.h_kv);
+      if (it.tree_lo != kNoTree) CHECK(use_tree && it.tree_lo >= 0 && it.kv_end - it.tree_lo <= kMaxTreeTokens);
       if (it.flags & kItemPartial) {
         CHECK(it.flag_id >= 0 && it.flag_id < h.num_flags && it.partial_row >= 0);
         flag_written[it.flag_id] = 1;
@@ -143,6 +161,10 @@ int main(int argc, char** argv) {
       }
     }
     CHECK(max_partial == res.num_partial_rows);
+    CHECK((h.off_alibi != 0) == !cfg.alibi_raw.empty());
+    CHECK((h.off_tree != 0) == use_tree);
+    if (h.off_alibi != 0) CHECK(h.off_alibi + 4 * int64_t(cfg.h_qo) <= n);
+    if (h.off_tree != 0) CHECK(h.off_tree + 8 * int64_t(total_qo) <= n && h.off_tree % 8 == 0);
     for (int32_t t = 0; t < h.num_merge; ++t) {
       MergeTask m;
       std::memcpy(&m, base + h.off_merge + int64_t(t) * sizeof(MergeTask), sizeof(m));
