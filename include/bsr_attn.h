@@ -202,6 +202,17 @@ int bsr_attn_plan_tree_mask(bsr_attn_t h, const int32_t* qo_indptr, const int32_
                             const int32_t* last_page_len, int32_t batch, const uint8_t* tree_mask,
                             void* workspace, void* host_staging, void* stream);
 
+/* bsr_attn_plan with one page list per request and KV head (Core mechanism 1 with
+ * the page table per KV head): KV head h of block row r reads the pages
+ * kv_indices[kv_indptr[r * H_kv + h] .. kv_indptr[r * H_kv + h + 1]), whose last
+ * page holds last_page_len[r] valid slots.  This is the plan of the pages kept
+ * by bsr_attn_quest_select (kv_indptr is then its out_indptr).  kv_indptr has
+ * batch * H_kv + 1 entries; max_total_kv bounds the keys of one KV head.  Same
+ * validation and staging/upload contract as bsr_attn_plan. */
+int bsr_attn_plan_head_pages(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* last_page_len, int32_t batch, void* workspace,
+                             void* host_staging, void* stream);
+
 /* Plan over several BSR sub-matrices of one KV matrix (Core mechanism 2).  A query
  * token's keys are the union of the keys of the block rows that cover it, in format
  * order; the formats must not overlap in keys (caller contract).  Causal, windowed
@@ -282,6 +293,40 @@ int bsr_attn_append_kv(const void* k_new, const void* v_new, const int32_t* appe
                        const int32_t* last_page_len, int32_t batch, int64_t total_new,
                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t dtype,
                        void* k_pool, void* v_pool, int64_t num_pages, void* stream);
+
+/* Quest-style page-budget sparse decode (Applicable scenarios item 5 of the
+ * explainer page; paper Appendix G.5): long-context decode keeps a budget of KV
+ * pages per step and attends over the kept pages only.  The page choice follows
+ * Quest's criterion (the pages name the method, not the rule):
+ *
+ * bsr_attn_page_summary writes, for every page of the page table (kv_indptr,
+ * kv_indices, last_page_len as for bsr_attn_run, kv_indptr[0] = 0, num_entries =
+ * kv_indptr[batch]) and every KV head, the elementwise minimum and maximum of the
+ * page's valid keys: k_min, k_max [num_pages, H_kv, D] in the pool's dtype (F32
+ * or BF16; exact).  Pages outside [0, num_pages) are skipped.  Run it when pages
+ * fill, not every step.
+ *
+ * bsr_attn_quest_select chooses the pages of one decode step.  q: [batch, H_qo,
+ * D] (one token per request).  A page's score for query head h is
+ * sum_d max(q_d min_d, q_d max_d), an upper bound of q.k over its keys; a KV head
+ * takes the largest score of its H_qo / H_kv query heads.  Per request and KV
+ * head the last page is always kept and the page_budget - 1 best other pages join
+ * it (ties to the earlier page); their page ids go, in logical order with the last
+ * page last, to out_indices[out_indptr[r * H_kv + h] ..], a list of
+ * min(n_pages(r), page_budget) ids that the caller sizes in out_indptr ([batch *
+ * H_kv + 1], device).  scores: caller scratch of H_kv * num_entries floats.
+ * max_pages bounds the pages of one request (at most 16385, else
+ * BSR_ERR_UNSUPPORTED).  Asynchronous, no allocation, capturable.  The kept pages
+ * then run through bsr_attn_plan_head_pages and bsr_attn_run. */
+int bsr_attn_page_summary(const void* k_pool, const int32_t* kv_indptr, const int32_t* kv_indices,
+                          const int32_t* last_page_len, int32_t batch, int64_t num_entries,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t dtype,
+                          int64_t num_pages, void* k_min, void* k_max, void* stream);
+int bsr_attn_quest_select(const void* q, const void* k_min, const void* k_max, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, int32_t batch, int64_t num_entries, int32_t max_pages,
+                          int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                          int64_t num_pages, int32_t page_budget, const int32_t* out_indptr,
+                          int32_t* out_indices, float* scores, void* stream);
 
 void bsr_attn_destroy(bsr_attn_t h);
 const char* bsr_attn_last_error(void);

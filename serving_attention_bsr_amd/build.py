@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["kernels_d64.hip", "kernels_d128.hip", "kernels_d256.hip", "kernels_d64_var.hip",
-               "kernels_d128_var.hip", "kernels_d256_var.hip", "merge_states.hip", "append_kv.hip", "run_static.hip"]
+               "kernels_d128_var.hip", "kernels_d256_var.hip", "merge_states.hip", "append_kv.hip", "run_static.hip",
+               "quest.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 # Matrix-core results and accumulators in ordinary vector registers: with more than

@@ -430,6 +430,55 @@ int bsr_attn_plan_tree_mask(bsr_attn_t h, const int32_t* qo_indptr, const int32_
   return finish_plan(h, rows, total_qo, false, workspace, host_staging, stream, &tree);
 }
 
+int bsr_attn_plan_head_pages(bsr_attn_t h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* last_page_len, int32_t batch, void* workspace, void* host_staging,
+                             void* stream) {
+  if (h == nullptr) return fail(BSR_ERR_INVALID_ARG, "handle is null");
+  if (batch < 0) return fail(BSR_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch > h->cfg.max_batch) return fail(BSR_ERR_CAPACITY, "batch exceeds max_batch");
+  if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr || last_page_len == nullptr))
+    return fail(BSR_ERR_INVALID_ARG, "index array is null");
+  const int32_t P = h->cfg.page_size;
+  const int32_t hk = h->cfg.num_kv_heads;
+  if (batch > 0 && qo_indptr[0] != 0) return fail(BSR_ERR_INVALID_ARG, "qo_indptr[0] must be 0");
+  if (batch > 0 && kv_indptr[0] < 0) return fail(BSR_ERR_INVALID_ARG, "kv_indptr[0] must be >= 0");
+  std::vector<BlockRow> rows;
+  rows.reserve(static_cast<size_t>(batch) * hk);
+  int64_t total_kv = 0;
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t lq = int64_t(qo_indptr[r + 1]) - qo_indptr[r];
+    if (lq < 0) return fail(BSR_ERR_INVALID_ARG, "qo_indptr must be non-decreasing");
+    for (int32_t head = 0; head < hk; ++head) {
+      const int64_t e = int64_t(r) * hk + head;
+      const int64_t np = int64_t(kv_indptr[e + 1]) - kv_indptr[e];
+      if (np < 0) return fail(BSR_ERR_INVALID_ARG, "kv_indptr must be non-decreasing");
+      int64_t lkv = 0;
+      if (np > 0) {
+        if (last_page_len[r] < 1 || last_page_len[r] > P)
+          return fail(BSR_ERR_INVALID_ARG, "last_page_len[" + std::to_string(r) + "] outside [1, page_size]");
+        lkv = (np - 1) * P + last_page_len[r];
+      }
+      if (lkv >= (int64_t(1) << 30)) return fail(BSR_ERR_UNSUPPORTED, "a block row holds 2^30 keys or more");
+      if (h->cfg.causal && lq > lkv)
+        return fail(BSR_ERR_INVALID_ARG, "causal block row " + std::to_string(r) + " has more queries than keys");
+      total_kv += lkv;
+      BlockRow br;
+      br.qo_begin = qo_indptr[r];
+      br.qo_len = static_cast<int32_t>(lq);
+      br.page_begin = kv_indptr[e];
+      br.kv_len = static_cast<int32_t>(lkv);
+      br.head = head;
+      rows.push_back(br);
+    }
+  }
+  const int32_t total_qo = batch > 0 ? qo_indptr[batch] : 0;
+  if (total_qo > h->cfg.max_total_qo) return fail(BSR_ERR_CAPACITY, "sum of query lengths exceeds max_total_qo");
+  // (per-head rows: a request's keys count once per KV head)
+  if (total_kv > h->cfg.max_total_kv * hk)
+    return fail(BSR_ERR_CAPACITY, "KV lengths exceed max_total_kv per KV head");
+  return finish_plan(h, rows, total_qo, false, workspace, host_staging, stream);
+}
+
 int bsr_attn_plan_composable(bsr_attn_t h, int32_t num_formats, const bsr_format* formats,
                              int32_t total_qo, void* workspace, void* host_staging, void* stream) {
   if (h == nullptr) return fail(BSR_ERR_INVALID_ARG, "handle is null");
@@ -593,6 +642,63 @@ int bsr_attn_append_kv(const void* k_new, const void* v_new, const int32_t* appe
                            num_kv_heads, static_cast<int32_t>(row_bytes), page_size, num_pages, k_pool, v_pool,
                            static_cast<hipStream_t>(stream)) != 0)
     return fail(BSR_ERR_HIP, "append_kv launch failed");
+  return BSR_OK;
+}
+
+extern int bsr_launch_page_summary(const void*, const int32_t*, const int32_t*, const int32_t*, int32_t, int64_t,
+                                   int32_t, int32_t, int32_t, int32_t, int64_t, void*, void*, hipStream_t);
+extern int bsr_launch_quest_select(const void*, const void*, const void*, const int32_t*, const int32_t*, int32_t,
+                                   int64_t, int32_t, int32_t, int32_t, int32_t, int64_t, int32_t, const int32_t*,
+                                   int32_t*, float*, hipStream_t);
+
+// Quest page choice: the select kernel keeps one request's candidate keys in LDS.
+constexpr int32_t kQuestMaxPages = 16384 + 1;
+
+int bsr_attn_page_summary(const void* k_pool, const int32_t* kv_indptr, const int32_t* kv_indices,
+                          const int32_t* last_page_len, int32_t batch, int64_t num_entries, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t page_size, int32_t dtype, int64_t num_pages, void* k_min,
+                          void* k_max, void* stream) {
+  if (batch < 0 || num_entries < 0 || num_pages < 0) return fail(BSR_ERR_INVALID_ARG, "negative size");
+  if (num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0)
+    return fail(BSR_ERR_INVALID_ARG, "num_kv_heads, head_dim and page_size must be > 0");
+  if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16)
+    return fail(BSR_ERR_UNSUPPORTED, "page summaries support F32 and BF16 pools");
+  if (batch == 0 || num_entries == 0) return BSR_OK;
+  if (k_pool == nullptr || kv_indptr == nullptr || kv_indices == nullptr || last_page_len == nullptr ||
+      k_min == nullptr || k_max == nullptr)
+    return fail(BSR_ERR_INVALID_ARG, "null device pointer");
+  if (bsr_launch_page_summary(k_pool, kv_indptr, kv_indices, last_page_len, batch, num_entries, num_kv_heads,
+                              head_dim, page_size, dtype == BSR_DTYPE_F32 ? 4 : 2, num_pages, k_min, k_max,
+                              static_cast<hipStream_t>(stream)) != 0)
+    return fail(BSR_ERR_HIP, "page_summary launch failed");
+  return BSR_OK;
+}
+
+int bsr_attn_quest_select(const void* q, const void* k_min, const void* k_max, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, int32_t batch, int64_t num_entries, int32_t max_pages,
+                          int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                          int64_t num_pages, int32_t page_budget, const int32_t* out_indptr, int32_t* out_indices,
+                          float* scores, void* stream) {
+  if (batch < 0 || num_entries < 0 || num_pages < 0 || max_pages < 0)
+    return fail(BSR_ERR_INVALID_ARG, "negative size");
+  if (num_qo_heads <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads != 0)
+    return fail(BSR_ERR_INVALID_ARG, "num_qo_heads must be a positive multiple of num_kv_heads");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(BSR_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16)
+    return fail(BSR_ERR_UNSUPPORTED, "the page choice supports F32 and BF16 queries and summaries");
+  if (page_budget < 1) return fail(BSR_ERR_INVALID_ARG, "page_budget must be >= 1");
+  if (max_pages > kQuestMaxPages)
+    return fail(BSR_ERR_UNSUPPORTED, "a request holds more than 16385 pages (the page choice keeps one "
+                                     "request's candidates on chip)");
+  if (batch == 0) return BSR_OK;
+  if (q == nullptr || k_min == nullptr || k_max == nullptr || kv_indptr == nullptr || kv_indices == nullptr ||
+      out_indptr == nullptr || out_indices == nullptr || (num_entries > 0 && scores == nullptr))
+    return fail(BSR_ERR_INVALID_ARG, "null device pointer");
+  if (bsr_launch_quest_select(q, k_min, k_max, kv_indptr, kv_indices, batch, num_entries, num_qo_heads,
+                              num_kv_heads, head_dim, dtype == BSR_DTYPE_F32 ? 4 : 2, num_pages, page_budget,
+                              out_indptr, out_indices, scores, static_cast<hipStream_t>(stream)) != 0)
+    return fail(BSR_ERR_HIP, "quest_select launch failed");
   return BSR_OK;
 }
 

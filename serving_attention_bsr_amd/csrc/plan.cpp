@@ -525,7 +525,10 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
     const bool wide = static_cast<int64_t>(r.qo_len) * g > kMaxDecodeRows;
     const bool mfma = cfg.bf16 && !cfg.kv8 && (kernel == kKindMfma || (kernel == kKindMixed && wide));
     const int32_t tile_tokens = (mfma ? q_tile : decode_rows) / g;
-    for (int32_t h = 0; h < h_kv; ++h) {
+    // a row with per-head pages serves its own KV head only
+    const int32_t h_first = r.head < 0 ? 0 : r.head;
+    const int32_t h_last = r.head < 0 ? h_kv : r.head + 1;
+    for (int32_t h = h_first; h < h_last; ++h) {
       for (int32_t t0 = 0; t0 < r.qo_len; t0 += tile_tokens) {
         Unit u;
         u.row = ri;

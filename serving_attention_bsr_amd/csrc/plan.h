@@ -50,6 +50,7 @@ struct BlockRow {
   int32_t kv_len = 0;
   int32_t format = 0;
   bool tree = false;  // the row's new tokens carry tree-mask rows
+  int32_t head = -1;  // the KV head this row's pages belong to, or -1 for every head
 };
 
 struct PlanResult {

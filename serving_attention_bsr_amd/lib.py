@@ -46,6 +46,9 @@ EXPORTED = [
     "bsr_attn_check",
     "bsr_attn_merge_states",
     "bsr_attn_append_kv",
+    "bsr_attn_plan_head_pages",
+    "bsr_attn_page_summary",
+    "bsr_attn_quest_select",
     "bsr_attn_destroy",
 ]
 
@@ -143,6 +146,10 @@ def load():
     lib.bsr_attn_merge_states.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p, c_i64, c_i32, vp]
     lib.bsr_attn_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, vp, vp,
                                        c_i64, vp]
+    lib.bsr_attn_plan_head_pages.argtypes = [vp, i32p, i32p, i32p, c_i32, vp, vp, vp]
+    lib.bsr_attn_page_summary.argtypes = [vp, vp, vp, vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i64, vp, vp, vp]
+    lib.bsr_attn_quest_select.argtypes = [vp, vp, vp, vp, vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64,
+                                          c_i32, vp, vp, vp, vp]
     lib.bsr_attn_destroy.argtypes = [vp]
     lib.bsr_attn_destroy.restype = None
     for name in EXPORTED:
@@ -268,6 +275,27 @@ def bsr_attn_append_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, last_
                                      stream))
 
 
+def bsr_attn_plan_head_pages(h, qo_indptr, kv_indptr_heads, last_page_len, workspace, host_staging, stream):
+    qo, kv, last = _i32(qo_indptr), _i32(kv_indptr_heads), _i32(last_page_len)
+    batch = len(qo) - 1
+    _check(load().bsr_attn_plan_head_pages(h, _ptr(qo), _ptr(kv), _ptr(last), batch, workspace, host_staging,
+                                           stream))
+
+
+def bsr_attn_page_summary(k_pool, kv_indptr, kv_indices, last_page_len, batch, num_entries, num_kv_heads, head_dim,
+                          page_size, dtype, num_pages, k_min, k_max, stream):
+    _check(load().bsr_attn_page_summary(k_pool, kv_indptr, kv_indices, last_page_len, batch, num_entries,
+                                        num_kv_heads, head_dim, page_size, dtype, num_pages, k_min, k_max, stream))
+
+
+def bsr_attn_quest_select(q, k_min, k_max, kv_indptr, kv_indices, batch, num_entries, max_pages, num_qo_heads,
+                          num_kv_heads, head_dim, dtype, num_pages, page_budget, out_indptr, out_indices, scores,
+                          stream):
+    _check(load().bsr_attn_quest_select(q, k_min, k_max, kv_indptr, kv_indices, batch, num_entries, max_pages,
+                                        num_qo_heads, num_kv_heads, head_dim, dtype, num_pages, page_budget,
+                                        out_indptr, out_indices, scores, stream))
+
+
 def bsr_attn_destroy(h):
     load().bsr_attn_destroy(h)
 
@@ -373,6 +401,13 @@ class BsrAttention:
         ws = self._ws_ptr if upload else None
         bsr_attn_plan_tree_mask(self.handle, qo_indptr, kv_indptr, last_page_len, pack_tree_masks(masks), ws,
                                 self._staging_ptr, self._stream())
+        return self.info()
+
+    def plan_head_pages(self, qo_indptr, kv_indptr_heads, last_page_len, upload=True):
+        """Plan with one page list per request and KV head (kv_indptr_heads: [B * H_kv + 1])."""
+        ws = self._ws_ptr if upload else None
+        bsr_attn_plan_head_pages(self.handle, qo_indptr, kv_indptr_heads, last_page_len, ws, self._staging_ptr,
+                                 self._stream())
         return self.info()
 
     def plan_composable(self, formats, total_qo):
@@ -481,3 +516,54 @@ def append_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, last_page_len,
         batch, total_new, h_kv, d, page_size, dtype, _dptr(k_pool), _dptr(v_pool), num_pages,
         _stream_ptr(torch.cuda.current_stream(k_pool.device)),
     )
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return BSR_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return BSR_DTYPE_F32
+    raise ValueError("dtype must be float32 or bfloat16")
+
+
+def quest_out_indptr(kv_indptr, num_kv_heads, page_budget):
+    """Host CSR of the kept page lists: min(n_pages(r), budget) ids per (request, KV head)."""
+    n = np.diff(np.asarray(kv_indptr, dtype=np.int64))
+    kept = np.repeat(np.minimum(n, page_budget), num_kv_heads)
+    return np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
+
+
+def page_summary(k_pool, kv_indptr, kv_indices, last_page_len, k_min=None, k_max=None):
+    """Per-page key min/max ([num_pages, H_kv, D], the pool's dtype) of a page table's pages."""
+    import torch
+
+    num_pages, h_kv, page_size, d = k_pool.shape
+    if k_min is None:
+        k_min = torch.zeros((num_pages, h_kv, d), dtype=k_pool.dtype, device=k_pool.device)
+    if k_max is None:
+        k_max = torch.zeros((num_pages, h_kv, d), dtype=k_pool.dtype, device=k_pool.device)
+    batch = kv_indptr.numel() - 1
+    bsr_attn_page_summary(_dptr(k_pool), _dptr(kv_indptr), _dptr(kv_indices), _dptr(last_page_len), batch,
+                          kv_indices.numel(), h_kv, d, page_size, _dtype_code(k_pool), num_pages, _dptr(k_min),
+                          _dptr(k_max), _stream_ptr(torch.cuda.current_stream(k_pool.device)))
+    return k_min, k_max
+
+
+def quest_select(q, k_min, k_max, kv_indptr, kv_indices, page_budget, out_indptr, max_pages, out_indices=None,
+                 scores=None):
+    """Kept page ids per (request, KV head) into out_indices (CSR out_indptr, device int32)."""
+    import torch
+
+    batch, h_qo, d = q.shape
+    num_pages, h_kv, _ = k_min.shape
+    entries = kv_indices.numel()
+    if out_indices is None:
+        out_indices = torch.empty(max(int(out_indptr[-1].item()), 1), dtype=torch.int32, device=q.device)
+    if scores is None:
+        scores = torch.empty(max(h_kv * entries, 1), dtype=torch.float32, device=q.device)
+    bsr_attn_quest_select(_dptr(q), _dptr(k_min), _dptr(k_max), _dptr(kv_indptr), _dptr(kv_indices), batch, entries,
+                          max_pages, h_qo, h_kv, d, _dtype_code(q), num_pages, page_budget, _dptr(out_indptr),
+                          _dptr(out_indices), _dptr(scores), _stream_ptr(torch.cuda.current_stream(q.device)))
+    return out_indices
