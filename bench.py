@@ -34,7 +34,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 HEADLINE = "batch_decode"
 ALL = ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill", "shared_prefix_composable",
-       "batch_decode_fp8", "batch_decode_window", "append_kv_prefill"]
+       "batch_decode_fp8", "batch_decode_window", "spec_decode_tree", "append_kv_prefill", "quest_sparse_decode"]
+# Quest-style page-budget decode: the step is the page choice plus attention
+QUEST = {"quest_sparse_decode": 64}  # page budget
 # writing the new K/V rows of a workload into its paged cache (not an attention run)
 APPEND = {"append_kv_prefill": "ragged_causal_prefill"}
 
@@ -173,6 +175,7 @@ def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
     )
     work = algorithmic_work(w, composable)
     out = dict(workload=name, dtype=w.dtype, bytes=work["bytes"], flops=work["flops"])
+    trees = W.draft_trees(w.qo_lens, 10) if name == "spec_decode_tree" else None
     try:
         torch.cuda.synchronize()
         plan_times = []
@@ -180,6 +183,8 @@ def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
             t0 = time.perf_counter()
             if composable:
                 info = h.plan_composable([f.as_dict() for f in w.formats], w.batch)
+            elif trees is not None:
+                info = h.plan_tree_mask(w.qo_indptr, w.kv_indptr, w.last_page_len, trees)
             else:
                 info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
             plan_times.append(time.perf_counter() - t0)
@@ -268,6 +273,84 @@ def bench_append(name, steps, warmup, flush, mode="read"):
                               frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)), None
 
 
+def bench_quest(name, steps, warmup, flush, mode="read", graph=True):
+    """Quest-style sparse decode at the page's shape: one step is the page choice
+    (scores from the per-page key summaries, top pages per request and KV head) and
+    attention over the kept pages (run() of the per-head plan, made once from the
+    lengths).  The summaries are built before timing: they change only when a page
+    fills.  Algorithmic bytes: the summaries (2 D elements per page and KV head),
+    the kept K/V, Q, O and LSE."""
+    import torch
+
+    from serving_attention_bsr_amd import lib
+    from serving_attention_bsr_amd import workloads as W
+
+    budget = QUEST[name]
+    print(f"[bench] {name}: building inputs", file=sys.stderr, flush=True)
+    w = W.named(name)
+    dev = torch.device("cuda:0")
+    q, k, v = w.q.to(dev), w.k_pool.to(dev), w.v_pool.to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    kvp, kvi, last = i32(w.kv_indptr), i32(w.kv_indices), i32(w.last_page_len)
+    kmin, kmax = lib.page_summary(k, kvp, kvi, last)
+    out_ptr_h = lib.quest_out_indptr(w.kv_indptr, w.num_kv_heads, budget)
+    out_ptr = i32(out_ptr_h)
+    out_idx = torch.empty(int(out_ptr_h[-1]), dtype=torch.int32, device=dev)
+    scores = torch.empty(w.num_kv_heads * len(w.kv_indices), dtype=torch.float32, device=dev)
+    n_max = int(np.diff(w.kv_indptr).max())
+    h = lib.BsrAttention(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, dtype=w.dtype,
+                         max_batch=w.batch, max_total_qo=w.batch, max_total_kv=int(w.kv_lens.max()), device=0)
+    plan_times = []
+    for _ in range(20):
+        t0 = time.perf_counter()
+        info = h.plan_head_pages(w.qo_indptr, out_ptr_h, w.last_page_len)
+        plan_times.append(time.perf_counter() - t0)
+    plan_us = float(np.median(plan_times) * 1e6)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lib.quest_select(q, kmin, kmax, kvp, kvi, budget, out_ptr, n_max, out_indices=out_idx, scores=scores)
+        h.run(q, k, v, out_idx, o, lse)
+
+    times, wall = timed_steps(step, steps, warmup, stream, flush, mode)
+    h.check()
+    med = float(np.median(times))
+    n_pages = int(np.diff(w.kv_indptr.astype(np.int64)).sum())
+    kept = int(out_ptr_h[-1])
+    kept_keys = 0
+    for r in range(w.batch):
+        n = int(w.kv_indptr[r + 1] - w.kv_indptr[r])
+        kept_keys += (min(n, budget) - 1) * w.page_size + int(w.last_page_len[r]) if n else 0
+    elt = 2
+    summary_bytes = 2 * n_pages * w.num_kv_heads * w.head_dim * elt
+    kv_bytes = 2 * kept_keys * w.num_kv_heads * w.head_dim * elt
+    qo_bytes = 2 * w.batch * w.num_qo_heads * w.head_dim * elt + 4 * w.batch * w.num_qo_heads
+    work_bytes = summary_bytes + kv_bytes + qo_bytes + 4 * (n_pages + kept)
+    gbs = work_bytes / (med * 1e-3) / 1e9
+    out = dict(workload=name, dtype=w.dtype, page_budget=budget, bytes=work_bytes, summary_bytes=summary_bytes,
+               kv_bytes=kv_bytes, ms_median=med, ms_min=float(times.min()), wall_s=wall, plan_us=plan_us,
+               plan=info, hbm_GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
+               roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None))
+    if graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                step()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step()
+            gt, _ = timed_steps(g.replay, steps, warmup, stream, flush, mode)
+            out["graph_ms_median"] = float(np.median(gt))
+        except Exception as exc:  # report, do not hide
+            out["graph_error"] = repr(exc)
+    return out, None
+
+
 def cpu_model():
     """The host CPU's model name from /proc/cpuinfo (None if not readable)."""
     try:
@@ -347,6 +430,8 @@ def main():
     for name in names:
         if name in APPEND:
             r, ctx = bench_append(name, args.steps, args.warmup, flush, mode=args.flush)
+        elif name in QUEST:
+            r, ctx = bench_quest(name, args.steps, args.warmup, flush, mode=args.flush, graph=not args.no_graph)
         else:
             r, ctx = bench_workload(name, args.steps, args.warmup, flush, graph=not args.no_graph,
                                     nwg=args.num_workgroups, mode=args.flush)

@@ -23,8 +23,9 @@
 //                        per lane; HBM-bound: 2 D elements of summaries per pair.
 //   quest_select_kernel  one workgroup per (request, KV head): the candidate
 //                        scores as order-preserving 32-bit keys in LDS, a 4-pass
-//                        8-bit radix select of the (budget - 1)-th largest key,
-//                        then an ordered scan that keeps every larger key and the
+//                        8-bit radix select of the (budget - 1)-th largest key
+//                        (histogram in LDS, bin search by a workgroup scan), then
+//                        ordered scans that keep every larger key and the
 //                        earliest equal ones.  Deterministic (LDS histogram counts
 //                        are exact integers; the output order is the index order).
 #include <hip/hip_runtime.h>
@@ -154,6 +155,26 @@ __global__ __launch_bounds__(kQuestThreads) void quest_score_kernel(const T* q, 
   if (live && sub == 0) scores[static_cast<int64_t>(hk) * entries + e] = in_pool ? best : -__builtin_inff();
 }
 
+// Exclusive prefix sum over the 256 threads of the workgroup, in thread order
+// (lane prefix by shuffles, then the wavefront totals through LDS); every thread
+// of the workgroup must call it.  tmp: 4 ints of LDS.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t x, int32_t* tmp) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int32_t inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  int32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += tmp[w];
+  __syncthreads();  // tmp is free for the next call
+  return before + inc - x;
+}
+
 // Order-preserving 32-bit key of a float (larger float, larger key).
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -165,10 +186,10 @@ __global__ __launch_bounds__(kQuestThreads) void quest_select_kernel(const float
                                                                     int64_t entries, int32_t budget,
                                                                     const int32_t* out_indptr,
                                                                     int32_t* out_indices) {
+  static_assert(kQuestThreads == 256, "one histogram bin per thread");
   __shared__ uint32_t keys[kQuestMaxCandidates];
   __shared__ uint32_t hist[256];
-  __shared__ int32_t scan_a[kQuestThreads];
-  __shared__ int32_t scan_b[kQuestThreads];
+  __shared__ int32_t scan_tmp[4];
   __shared__ uint32_t shared_digit;
   __shared__ int32_t shared_krem;
   const int tid = threadIdx.x;
@@ -199,18 +220,12 @@ __global__ __launch_bounds__(kQuestThreads) void quest_select_kernel(const float
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int32_t above = 0;
-      uint32_t digit = 0;
-      for (int b = 255; b >= 0; --b) {
-        const int32_t c = static_cast<int32_t>(hist[b]);
-        if (above + c >= krem) {
-          digit = static_cast<uint32_t>(b);
-          break;
-        }
-        above += c;
-      }
-      shared_digit = digit;
+    // thread t holds bin 255 - t: its exclusive prefix counts the keys in higher
+    // bins; exactly one bin holds the k-th largest key
+    const int32_t c = static_cast<int32_t>(hist[255 - tid]);
+    const int32_t above = block_exclusive_scan(c, scan_tmp);
+    if (above < krem && krem <= above + c) {
+      shared_digit = static_cast<uint32_t>(255 - tid);
       shared_krem = krem - above;
     }
     __syncthreads();
@@ -228,30 +243,11 @@ __global__ __launch_bounds__(kQuestThreads) void quest_select_kernel(const float
     gt += keys[i] > thr;
     eq += keys[i] == thr;
   }
-  scan_a[tid] = eq;
-  __syncthreads();
-  if (tid == 0) {  // exclusive scan of the equal counts
-    int32_t run = 0;
-    for (int t = 0; t < kQuestThreads; ++t) {
-      const int32_t c = scan_a[t];
-      scan_a[t] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  const int32_t take = max(0, min(eq, krem - scan_a[tid]));  // equal keys this thread keeps
-  scan_b[tid] = gt + take;
-  __syncthreads();
-  if (tid == 0) {  // exclusive scan of the kept counts: output positions
-    int32_t run = 0;
-    for (int t = 0; t < kQuestThreads; ++t) {
-      const int32_t c = scan_b[t];
-      scan_b[t] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  int32_t pos = scan_b[tid];
+  // equal keys before this thread's run, then this thread's kept count and its
+  // first output position
+  const int32_t eq_before = block_exclusive_scan(eq, scan_tmp);
+  const int32_t take = max(0, min(eq, krem - eq_before));  // equal keys this thread keeps
+  int32_t pos = block_exclusive_scan(gt + take, scan_tmp);
   int32_t eq_left = take;
   for (int32_t i = i0; i < i1; ++i) {
     const uint32_t key = keys[i];

@@ -345,6 +345,45 @@ def shared_prefix_composable(
     )
 
 
+def quest_sparse_decode(seed=8, batch=1, seq=32768, page_size=16, num_heads=32, head_dim=128, tensors=True):
+    """Long-context decode for Quest-style page budgets: the shape the explainer
+    page quotes (sequence 32768, pages of 16 keys, 32 query and 32 KV heads, head
+    dim 128), bf16, one query token per request."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return build("quest_sparse_decode", seed, [1] * batch, [seq] * batch, page_size, num_heads, num_heads, head_dim,
+                 dtype="bf16", rng=rng, tensors=tensors)
+
+
+def spec_decode_tree(seed=9, batch=32, lo=512, hi=8192, draft_lo=2, draft_hi=8, tensors=True):
+    """Speculative decoding with token trees: batch decode shapes (32/8 heads,
+    D=128, P=16, KV U[lo, hi]) with U[draft_lo, draft_hi] draft tokens per request
+    that are the request's last keys; the tree masks are drawn by the caller."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kv = rng.integers(lo, hi, size=batch, endpoint=True)
+    qo = rng.integers(draft_lo, draft_hi, size=batch, endpoint=True)
+    return build("spec_decode_tree", seed, qo, kv, 16, 32, 8, 128, dtype="bf16", causal=True, rng=rng,
+                 tensors=tensors)
+
+
+def draft_trees(qo_lens, seed):
+    """Token trees for speculative decoding, one boolean [n, n] matrix per request:
+    draft token t (t > 0) hangs under a uniformly drawn earlier token or under the
+    accepted prefix, and sees itself and its ancestors."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    trees = []
+    for n in qo_lens:
+        n = int(n)
+        parent = [-1] + [int(rng.integers(-1, t)) for t in range(1, n)]
+        m = np.zeros((n, n), dtype=bool)
+        for t in range(n):
+            u = t
+            while u >= 0:
+                m[t, u] = True
+                u = parent[u]
+        trees.append(m)
+    return trees
+
+
 NAMED = {
     "tiny_decode_f32": tiny_decode_f32,
     "batch_decode": batch_decode,
@@ -353,6 +392,8 @@ NAMED = {
     "skewed_long_decode": skewed_long_decode,
     "ragged_causal_prefill": ragged_causal_prefill,
     "shared_prefix_composable": shared_prefix_composable,
+    "quest_sparse_decode": quest_sparse_decode,
+    "spec_decode_tree": spec_decode_tree,
 }
 
 

@@ -80,3 +80,19 @@ def test_variant_split_plan_repeats_bitwise():
     info = _run(("repeat_tree_alibi", [2, 2, 48], [9000, 300, 4000], 32, 8, 128, 16, "bf16", True, 0.0, 0, 32, True,
                  True), repeat=5)
     assert info["num_partial_items"] > 0
+
+
+def test_named_spec_decode_tree():
+    """The tree-masked speculative-decoding workload the benchmark times, in full."""
+    say("workload spec_decode_tree")
+    w = W.named("spec_decode_tree")
+    trees = W.draft_trees(w.qo_lens, 10)
+    h = handle_for(w)
+    q, k, v, idx = to_gpu(w)
+    info = h.plan_tree_mask(w.qo_indptr, w.kv_indptr, w.last_page_len, trees)
+    say("plan", info)
+    o, lse = h.run(q, k, v, idx)
+    torch.cuda.synchronize()
+    h.check()
+    ro, rl = oracle_of(w, tree_masks=trees)
+    compare(w, o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "spec_decode_tree")
