@@ -34,7 +34,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 HEADLINE = "batch_decode"
 ALL = ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "ragged_causal_prefill", "shared_prefix_composable",
-       "batch_decode_fp8", "batch_decode_window", "spec_decode_tree", "append_kv_prefill", "quest_sparse_decode"]
+       "batch_decode_fp8", "ragged_causal_prefill_fp8", "batch_decode_window", "spec_decode_tree", "append_kv_prefill",
+       "quest_sparse_decode"]
+# workloads bound by the matrix cores (the rest by HBM)
+MFMA_BOUND = ("ragged_causal_prefill", "ragged_causal_prefill_fp8")
 # Quest-style page-budget decode: the step is the page choice plus attention
 QUEST = {"quest_sparse_decode": 64}  # page budget
 # writing the new K/V rows of a workload into its paged cache (not an attention run)
@@ -217,7 +220,7 @@ def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
     out["mfma_frac"] = tfl / BF16_MFMA_PEAK_TFLOPS
     # prefill is bound by the matrix cores; decode and the shared-prefix batch
     # (whose prefix is read once for all branches) by HBM
-    out["roofline"] = roofline(work, med, recorded_traffic(name), mfma=name == "ragged_causal_prefill")
+    out["roofline"] = roofline(work, med, recorded_traffic(name), mfma=name in MFMA_BOUND)
     if graph:
         try:
             s = torch.cuda.Stream()

@@ -87,9 +87,11 @@ typedef enum bsr_status {
 } bsr_status;
 
 /* BSR_DTYPE_BF16_KV_FP8: Q and O bf16, K and V pools (and appended K/V rows) OCP
- * FP8 E4M3 codes, one byte per element; the decode body only (query rows of more
- * than 8 folded rows run as 8-row decode tiles).  Scales are the caller's: a K
- * scale folds into sm_scale, a V scale multiplies O. */
+ * FP8 E4M3 codes, one byte per element (Core mechanism 8 of the explainer page,
+ * paper Appendix F), converted exactly to bf16 on chip; decode rows on the VALU
+ * body, wide rows (prefill) on the MFMA tile body up to head dim 128 (at 256 they
+ * run as 8-row decode tiles).  Scales are the caller's: a K scale folds into
+ * sm_scale, a V scale multiplies O. */
 typedef enum bsr_dtype { BSR_DTYPE_F32 = 0, BSR_DTYPE_BF16 = 1, BSR_DTYPE_BF16_KV_FP8 = 2 } bsr_dtype;
 
 typedef struct bsr_attn_config {

@@ -99,6 +99,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(stride), 0x7fffffff,
                                            0x00020000);
 }
+// Two OCP FP8 E4M3 codes (the low or high 16 bits of w) as a bf16 pair, exactly
+// (E4M3 values are bf16 values): the gfx950 scaled conversion with scale 1, whose
+// decoding of all 256 codes was checked against the format on the GPU.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);

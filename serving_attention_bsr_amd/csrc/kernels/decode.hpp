@@ -140,13 +140,6 @@ struct DecodeBody {
     }
   }
 
-  // Two E4M3 codes (the low or high half of w) as a bf16 pair (exact).
-  // (gfx950 scaled conversion with scale 1: exact for all 256 codes, checked on
-  // the GPU against the format)
-  template <bool HIGH>
-  static __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
-  }
 
   static __device__ __forceinline__ float dot_row(const uint4 (&q)[QLD], const uint4 (&k)[NLD]) {
     float s = 0.0f;

@@ -51,20 +51,22 @@ inline void add_decode_kv8(std::vector<KernelEntry>* out) {
 template <int D>
 constexpr int kMfmaOcc = 2;
 
-template <int D, bool CAP, bool PAGE1, bool VAR>
+template <int D, bool CAP, bool PAGE1, bool VAR, bool KV8 = false>
 inline void add_mfma(std::vector<KernelEntry>* out) {
-  out->push_back({KernelKey{kKindMfma, true, D, 0, CAP, PAGE1, false, VAR},
+  out->push_back({KernelKey{kKindMfma, true, D, 0, CAP, PAGE1, KV8, VAR},
                   reinterpret_cast<const void*>(
-                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, kMfmaOcc<D>, PAGE1, false,
+                      &bsr_persistent_kernel<D, true, 4, kDecodeTb<true>, CAP, kKindMfma, kMfmaOcc<D>, PAGE1, KV8,
                                              VAR>),
                   kMfmaOcc<D>});
 }
 
-template <int D, int ROWS, bool CAP, bool VAR>
+// (an FP8 cache's decode body takes four KV rows per lane group and step)
+template <int D, int ROWS, bool CAP, bool VAR, bool KV8 = false>
 inline void add_mixed(std::vector<KernelEntry>* out) {
-  out->push_back({KernelKey{kKindMixed, true, D, ROWS, CAP, false, false, VAR},
+  out->push_back({KernelKey{kKindMixed, true, D, ROWS, CAP, false, KV8, VAR},
                   reinterpret_cast<const void*>(
-                      &bsr_persistent_kernel<D, true, ROWS, kDecodeTb<true>, CAP, kKindMixed, 1, false, false, VAR>),
+                      &bsr_persistent_kernel<D, true, ROWS, (KV8 ? 2 : 1) * kDecodeTb<true>, CAP, kKindMixed, 1,
+                                             false, KV8, VAR>),
                   1});
 }
 
@@ -93,6 +95,17 @@ inline void register_head_dim(std::vector<KernelEntry>* out) {
   add_decode_kv8<D, 4, true, VAR>(out);
   add_decode_kv8<D, 8, false, VAR>(out);
   add_decode_kv8<D, 8, true, VAR>(out);
+  if constexpr (D <= 128) {
+    // FP8 K/V on the 32-row MFMA body (prefill and wide rows)
+    add_mfma<D, false, false, VAR, true>(out);
+    add_mfma<D, true, false, VAR, true>(out);
+    add_mfma<D, false, true, VAR, true>(out);
+    add_mfma<D, true, true, VAR, true>(out);
+    add_mixed<D, 4, false, VAR, true>(out);
+    add_mixed<D, 4, true, VAR, true>(out);
+    add_mixed<D, 8, false, VAR, true>(out);
+    add_mixed<D, 8, true, VAR, true>(out);
+  }
 }
 
 }  // namespace bsr

@@ -40,10 +40,11 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 template <int D, bool BF16, int ROWS, int TB, bool CAP, int KIND, bool PAGE1, bool KV8, bool VAR>
 struct PersistentKernel {
   static_assert(KIND == kKindDecode || BF16, "the MFMA body is bf16 only");
-  static_assert(KIND == kKindDecode || !KV8, "an FP8 K/V cache runs on the decode body only");
+  static_assert(KIND == kKindDecode || !KV8 || D <= 128, "an FP8 K/V cache runs on the 32-row MFMA body only");
   using Decode = DecodeBody<D, BF16, ROWS, TB, CAP, KV8, VAR>;
   // 32 rows per wavefront up to D = 128; 16 rows (two workgroups per CU) at D = 256
-  using Mfma = typename std::conditional<D == 256, MfmaBody16<D, CAP, PAGE1, VAR>, MfmaBody<D, CAP, PAGE1, VAR>>::type;
+  using Mfma =
+      typename std::conditional<D == 256, MfmaBody16<D, CAP, PAGE1, VAR>, MfmaBody<D, CAP, PAGE1, VAR, KV8>>::type;
   using Merge = MergeBody<D, BF16>;
   static constexpr int LDS_FLOATS =
       cmax(Merge::LDS_FLOATS, cmax(KIND == kKindMfma ? 0 : Decode::LDS_FLOATS,

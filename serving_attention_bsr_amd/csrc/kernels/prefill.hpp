@@ -42,31 +42,65 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 // PAGE1: every page holds one key (page size 1, the radix-tree layout), so a key's
 // page is its own position and no division is needed.
 // VAR: the plan may carry ALiBi slopes and tree masks.
-template <int D, bool CAP, bool PAGE1 = false, bool VAR = false>
+// KV8: K and V are OCP FP8 E4M3 codes (Q and O bf16; Appendix F of the paper, as
+// the explainer page's Core mechanism 8 restates it: an FP8 cache with 16-bit
+// queries, codes converted on chip).  Tiles then hold one byte per element (half
+// the gather), and each operand read converts its 8 codes to bf16 exactly before
+// the bf16 products: K rows with 8-byte reads, V^T with the gfx950 8-bit
+// transpose read.
+template <int D, bool CAP, bool PAGE1 = false, bool VAR = false, bool KV8 = false>
 struct MfmaBody {
   static constexpr int BR = 128;           // folded rows per item
   static constexpr int BC = 64;            // keys per tile
   static constexpr int KB = BC / 32;       // 32-key blocks per tile
   static constexpr int DK = D / 16;        // MFMA k-steps over D for S^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
-  static constexpr int NCH = D / 8;        // 16-byte chunks per row
+  static constexpr int RB = KV8 ? D : 2 * D;  // bytes of one K/V row
+  static constexpr int NCH = RB / 16;      // 16-byte chunks per row
   static constexpr int RPI = 64 / NCH;     // rows per 1 KB gather instruction
   static constexpr int NI = BC / RPI / kWaves;  // gather instructions per wavefront, tile and matrix
-  // Tiles are unpadded (row r at r * D elements, K then V) with the 16-byte chunks
+  // Tiles are unpadded (row r at r * RB bytes, K then V) with the 16-byte chunks
   // of each row permuted: chunk c of row r sits in slot c ^ swz(r), which keeps every
-  // gather instruction a contiguous 1 KB of LDS.  K is read one row per lane, 16
-  // lanes per pass, all at one chunk: swz_k puts 16 consecutive rows on the 16
-  // slots of 256 bytes (all 64 banks).  V is read with the transpose read, 4
+  // gather instruction a contiguous 1 KB of LDS.  bf16: K is read one row per
+  // lane, 16 lanes per pass, all at one chunk: swz_k puts 16 consecutive rows on the
+  // 16 slots of 256 bytes (all 64 banks).  V is read with the transpose read, 4
   // consecutive keys x 64 bytes per half-wave: swz_v puts the 4 rows' 64-byte groups
-  // on 4 distinct quarters of the banks.
-  static constexpr int STAGE = 2 * BC * D;  // bf16 elements of one buffer
+  // on 4 distinct quarters of the banks.  FP8: see swz8.
+  static constexpr int STAGE = 2 * BC * RB / 2;  // one buffer (K then V tile), in 16-bit units
+  static constexpr int VOFF = BC * RB / 2;       // V tile inside a buffer, in 16-bit units
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
   static_assert(D == 64 || D == 128, "head_dim (D = 256 uses the 16-row body)");
   static_assert(NI * RPI * kWaves == BC, "whole gather instructions per wavefront");
 
-  static __device__ __forceinline__ int swz_k(int r) { return (r / (16 / NCH)) % NCH; }
-  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / (16 / NCH)) % (NCH / 4)); }
+  // FP8 tiles (rows of D bytes): the K read of a half-wave takes 8 bytes at one
+  // chunk of 32 consecutive rows, the V transpose read of a half-wave takes 2 x 8
+  // bytes of two adjacent chunks from rows r0 + {0, 1, 2, 3, 8, 9, 10, 11}.  The
+  // permutation below spreads the V read over all 64 banks and the K read over 16
+  // slots (two rows per slot, the fewest 16-byte granularity allows): at D = 128
+  // rows of one parity (same 128-byte half of 256 bytes) get slot bits (r2, r1, r3),
+  // at D = 64 rows of one residue mod 4 get (r3, r2).
+  static __device__ __forceinline__ int swz8(int r) {
+    if constexpr (D == 128)
+      return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2);
+    else
+      return ((r >> 2) & 1) | (((r >> 3) & 1) << 1);
+  }
+  static __device__ __forceinline__ int swz_k(int r) {
+    if constexpr (KV8) return swz8(r);
+    return (r / (16 / NCH)) % NCH;
+  }
+  static __device__ __forceinline__ int swz_v(int r) {
+    if constexpr (KV8) return swz8(r);
+    return 4 * ((r / (16 / NCH)) % (NCH / 4));
+  }
+
+  // Eight FP8 codes (in order) as the bf16x8 operand of one product.
+  static __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint2 w) {
+    const u32x4_t v = {e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x), e4m3x2_to_bf16x2<false>(w.y),
+                       e4m3x2_to_bf16x2<true>(w.y)};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
 
   // Page ids of this lane's rows, loaded a tile ahead of the rows themselves.  The
   // id is kept as loaded and the row index formed only when the rows are gathered:
@@ -102,7 +136,7 @@ struct MfmaBody {
   }
 
   // Gather this lane's rows N0 <= n < N1 of a tile's K and V into the buffer at LDS
-  // byte address buf (K at buf, V at buf + 2 BC D).  rows_per_page = H_kv * P: pool
+  // byte address buf (K at buf, V at buf + BC RB).  rows_per_page = H_kv * P: pool
   // rows between consecutive pages.
   static __device__ __forceinline__ void gather(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                                 uint32_t rows_per_page, const Rows& rows, uint32_t buf, int wave,
@@ -115,13 +149,23 @@ struct MfmaBody {
       const int row = static_cast<int>(rows.page[n] * rows_per_page + rows.off[n]);
       const uint32_t dst = buf + static_cast<uint32_t>(NI * wave + n) * 1024u;
       lds_gather_b128(kr, dst, row, 16 * (slot ^ swz_k(r)));
-      lds_gather_b128(vr, dst + BC * D * 2, row, 16 * (slot ^ swz_v(r)));
+      lds_gather_b128(vr, dst + BC * RB, row, 16 * (slot ^ swz_v(r)));
     }
   }
 
   // Transpose read of 4 bf16 (one 8-byte half of a 16-byte chunk).
   static __device__ __forceinline__ i16x4_t read_tr(const uint16_t* addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const_cast<uint16_t*>(addr)));
+  }
+
+  // 8-bit transpose read (FP8 V tiles).  Measured on gfx950 with an in-bounds
+  // probe: within each 16-lane group, lane l receives as byte e (e = 0..7) byte
+  // l & 7 of the 8 bytes addressed by lane 2 e + (l & 15) / 8 of its group.
+  typedef int i32x2_t_ __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2_t_ lds_i32x2_t;
+  static __device__ __forceinline__ uint2 read_tr8(const uint8_t* addr) {
+    const i32x2_t_ v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(const_cast<uint8_t*>(addr)));
+    return make_uint2(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]));
   }
 
   // ---- pieces of one tile step -------------------------------------------------
@@ -140,8 +184,15 @@ struct MfmaBody {
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
         const int r = 32 * kb + col;   // swz_k(r) == swz_k(col): 32 rows apart
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + r * D + 8 * ((2 * ks + half) ^ swz_k(col))));
+        bf16x8_t a;
+        if constexpr (KV8) {
+          // elements 16 ks + 8 half .. + 7 of the row: 8 bytes of chunk ks
+          const uint8_t* lkb = reinterpret_cast<const uint8_t*>(lk);
+          a = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(lkb + r * RB + 16 * (ks ^ swz_k(col)) + 8 * half));
+        } else {
+          a = __builtin_bit_cast(bf16x8_t,
+                                 *reinterpret_cast<const u32x4_t*>(lk + r * D + 8 * ((2 * ks + half) ^ swz_k(col))));
+        }
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
         if ((ks + 1) % (DK / 2) == 0) hook(2 * kb + (ks + 1) / (DK / 2) - 1);
       }
@@ -240,6 +291,28 @@ struct MfmaBody {
   // d = 32 db + 16 (group & 1) + 4 (s & 3): key_off and d_off below.
   static __device__ __forceinline__ void pv(const uint16_t* lv, const bf16x8_t (&pb)[KB][2], int key_off,
                                             int d_off, f32x16_t (&acc)[DB]) {
+    if constexpr (KV8) {
+      // One 8-bit transpose read per product: addressing lane a (= lane % 16) of
+      // group G (= lane / 16) points at key 32 kb + 16 st + key_off (key_off =
+      // 8 (e / 4) + 4 half + e % 4 for e = a / 2) and at bytes 8 (a % 2) of chunk
+      // 2 db + G % 2, so lane (d = 32 db + lane % 32, half) receives V at d for the 8
+      // keys of its P registers, in their order.  d_off: 8 (a % 2) + chunk parity.
+      const uint8_t* lvb = reinterpret_cast<const uint8_t*>(lv);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int r = 32 * kb + 16 * st + key_off;  // swz_v(r) == swz_v(key_off)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int at = r * RB + 16 * ((2 * db + (d_off & 1)) ^ swz_v(key_off)) + (d_off & 8);
+            const bf16x8_t a = fp8x8_to_bf16x8(read_tr8(lvb + at));
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][st], acc[db], 0, 0, 0);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -273,8 +346,13 @@ struct MfmaBody {
     const int rho = wave * 32 + col;                  // folded row of this lane's column
     const bool row_ok = rho < rows_valid;
     const int t_local = rho / g;
-    const int key_off = 4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2);
-    const int d_off = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // addresses of the V^T operand reads (see pv): bf16, key and element offsets of
+    // the 16-bit transpose read; FP8, key of this addressing lane and, packed, its
+    // byte half (8 (a % 2)) and chunk parity (G % 2)
+    const int a16 = lane & 15;
+    const int key_off = KV8 ? 8 * ((a16 >> 1) >> 2) + 4 * (lane >> 5) + ((a16 >> 1) & 3)
+                            : 4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2);
+    const int d_off = KV8 ? 8 * (a16 & 1) + ((lane >> 4) & 1) : 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     // variant state of this lane's row: ALiBi slope and position, tree-mask row
     const bool alibi = VAR && var.has_alibi;
     const float slope = alibi && row_ok ? var.alibi[it.kv_head * g + rho % g] : 0.0f;
@@ -308,8 +386,8 @@ struct MfmaBody {
 
     const int ntok = it.kv_end - it.kv_begin;
     const int ntiles = (ntok + BC - 1) / BC;
-    const __amdgpu_buffer_rsrc_t krs = row_rsrc(p.k_pool, D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, D * 2);
+    const __amdgpu_buffer_rsrc_t krs = row_rsrc(p.k_pool, RB);
+    const __amdgpu_buffer_rsrc_t vrs = row_rsrc(p.v_pool, RB);
     const __amdgpu_buffer_rsrc_t irs = row_rsrc(p.kv_indices, 0);
     const uint32_t rpp = static_cast<uint32_t>(p.h_kv * p.page_size);
     Rows rows;
@@ -347,7 +425,7 @@ struct MfmaBody {
       bf16x8_t pb[KB][2];
       const float alpha = softmax(s, c, m_run, l_run, pb);
       rescale(alpha, acc);
-      pv(lk + BC * D, pb, key_off, d_off, acc);
+      pv(lk + VOFF, pb, key_off, d_off, acc);
     };
     // tiles in pairs, so that each step's buffers sit at fixed LDS offsets (the
     // reads then take them as immediate offsets instead of per-tile address math)

@@ -475,10 +475,12 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   int32_t kernel = kKindDecode;
   int32_t decode_rows = max_decode_rows <= 4 ? 4 : 8;
   int32_t q_tile = decode_rows;
+  // the MFMA bodies take bf16 K/V, and FP8 K/V up to head dim 128
+  const bool mfma_ok = cfg.bf16 && !(cfg.kv8 && cfg.head_dim > 128);
   if (any_wide) {
-    if (!cfg.bf16 || cfg.kv8) {
-      // fp32 and an FP8 K/V cache have no MFMA body here: long query rows run as
-      // tiles of 8 folded rows
+    if (!mfma_ok) {
+      // fp32, and an FP8 K/V cache at head dim 256, have no MFMA body here: long
+      // query rows run as tiles of 8 folded rows
       if (g > kMaxDecodeRows) {
         *err = "fp32 or FP8 K/V with more than 8 query heads per KV head is not supported";
         return BSR_ERR_UNSUPPORTED;
@@ -523,7 +525,7 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
     const BlockRow& r = rows[ri];
     if (r.qo_len == 0) continue;
     const bool wide = static_cast<int64_t>(r.qo_len) * g > kMaxDecodeRows;
-    const bool mfma = cfg.bf16 && !cfg.kv8 && (kernel == kKindMfma || (kernel == kKindMixed && wide));
+    const bool mfma = mfma_ok && (kernel == kKindMfma || (kernel == kKindMixed && wide));
     const int32_t tile_tokens = (mfma ? q_tile : decode_rows) / g;
     // a row with per-head pages serves its own KV head only
     const int32_t h_first = r.head < 0 ? 0 : r.head;

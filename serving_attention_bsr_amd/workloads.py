@@ -271,6 +271,18 @@ def ragged_causal_prefill(seed=4, batch=8, qo_lo=128, qo_hi=4096, pre_lo=0, pre_
     )
 
 
+def ragged_causal_prefill_fp8(seed=11, batch=8, qo_lo=128, qo_hi=4096, pre_lo=0, pre_hi=4096, tensors=True):
+    """The ragged causal prefill shapes (P=1, 32/8 heads, D=128) over an FP8 (E4M3)
+    K/V cache with bf16 queries and outputs."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    qo = rng.integers(qo_lo, qo_hi, size=batch, endpoint=True)
+    prefix = rng.integers(pre_lo, pre_hi, size=batch, endpoint=True)
+    return build(
+        "ragged_causal_prefill_fp8", seed, qo, prefix + qo, 1, 32, 8, 128, dtype=KV_FP8, causal=True, rng=rng,
+        tensors=tensors,
+    )
+
+
 def shared_prefix_composable(
     seed=5, branches=64, prefix_len=8192, suf_lo=64, suf_hi=512, page_size=16,
     num_qo_heads=32, num_kv_heads=8, head_dim=256, dtype="bf16", tensors=True,
@@ -392,6 +404,7 @@ NAMED = {
     "skewed_long_decode": skewed_long_decode,
     "ragged_causal_prefill": ragged_causal_prefill,
     "shared_prefix_composable": shared_prefix_composable,
+    "ragged_causal_prefill_fp8": ragged_causal_prefill_fp8,
     "quest_sparse_decode": quest_sparse_decode,
     "spec_decode_tree": spec_decode_tree,
 }

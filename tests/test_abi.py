@@ -81,12 +81,15 @@ def test_create_rejects_bad_slot2_speed():
                          slot2_speed=ok).close()
 
 
-def test_fp8_kv_handle_plans_decode_only():
-    """An FP8 K/V handle plans every query row on the decode body (8-row tiles for
-    long rows): the plan never uses the MFMA kinds."""
-    h = lib.BsrAttention(8, 2, 64, 16, dtype="bf16_kv_fp8", num_workgroups=8, device=-1, max_batch=4,
-                         max_total_qo=64, max_total_kv=4096, causal=True)
-    info = h.plan(np.array([0, 1, 41], dtype=np.int32), np.array([0, 4, 8], dtype=np.int32),
-                  np.array([16, 16], dtype=np.int32))
-    assert info["kernel"] == 1 and info["q_tile"] == 8
-    h.close()
+def test_fp8_kv_handle_kernel_choice():
+    """An FP8 K/V handle runs wide query rows on the MFMA tile body up to head dim
+    128 (a decode row next to them makes the mixed kind); at head dim 256 every row
+    runs on the decode body, long rows as 8-row tiles."""
+    qo, kv, last = (np.array([0, 1, 41], dtype=np.int32), np.array([0, 4, 8], dtype=np.int32),
+                    np.array([16, 16], dtype=np.int32))
+    for d, kind, tile in ((64, lib.KERNEL_MIXED, 128), (128, lib.KERNEL_MIXED, 128), (256, lib.KERNEL_DECODE, 8)):
+        h = lib.BsrAttention(8, 2, d, 16, dtype="bf16_kv_fp8", num_workgroups=8, device=-1, max_batch=4,
+                             max_total_qo=64, max_total_kv=4096, causal=True)
+        info = h.plan(qo, kv, last)
+        assert info["kernel"] == kind and info["q_tile"] == tile, (d, info)
+        h.close()

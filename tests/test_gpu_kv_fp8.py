@@ -3,8 +3,10 @@
 The oracle decodes the same E4M3 codes the GPU reads (oracle.decode_e4m3, pinned
 against the format) and runs the plain attention definition; the tolerance is the
 bf16 one.  Cases: head dims 64 / 128 / 256, split chunks with a soft-cap, 8-row
-speculative decode, wide query rows that run as 8-row decode tiles, and the
-batch decode workload with an FP8 cache.
+speculative decode, wide query rows on the MFMA tile body (head dims 64 and 128:
+causal, one-key pages, soft-cap, splits, a mixed grid) or as 8-row decode tiles
+(head dim 256), the batch decode workload and the ragged causal prefill with an
+FP8 cache.
 """
 
 import pytest
@@ -20,7 +22,15 @@ CASES = [
     ("kv8_d64_split_cap", [1] * 4, [17, 64, 100, 2550], 8, 2, 64, 16, False, 5.0, 16),
     ("kv8_d256_p7_split", [1] * 3, [10, 300, 900], 16, 4, 256, 7, False, 0.0, 8),
     ("kv8_rows8_spec_causal", [2, 2, 1], [90, 333, 5], 8, 2, 128, 16, True, 0.0, 0),
-    ("kv8_wide_rows_decode_tiles", [20, 3], [40, 300], 8, 2, 64, 16, True, 0.0, 8),
+    # wide rows at head dim 256 still run as 8-row decode tiles
+    ("kv8_d256_wide_rows_decode_tiles", [20, 3], [40, 300], 8, 2, 256, 16, True, 0.0, 8),
+    # FP8 on the 32-row MFMA tile body (head dims 64 and 128)
+    ("kv8_mfma_d64_causal_split", [20, 3], [40, 300], 8, 2, 64, 16, True, 0.0, 8),
+    ("kv8_mfma_d128_causal_p1", [300, 77, 1000], [700, 77, 1500], 32, 8, 128, 1, True, 0.0, 0),
+    ("kv8_mfma_d128_p16_cap_split", [64, 100], [6000, 3000], 32, 8, 128, 16, True, 30.0, 64),
+    ("kv8_mfma_d64_p3_noncausal", [129, 64], [65, 300], 4, 4, 64, 3, False, 0.0, 0),
+    ("kv8_mfma_d128_g8_p1_cap", [60, 200], [60, 900], 16, 2, 128, 1, False, 20.0, 0),
+    ("kv8_mixed_decode_prefill", [1, 50, 1, 3], [500, 120, 77, 3], 32, 8, 128, 4, True, 0.0, 16),
 ]
 
 
@@ -65,3 +75,13 @@ def test_kv_fp8_repeat_is_bitwise():
         else:
             assert torch.equal(o.view(torch.int16), first[0].view(torch.int16)), rep
             assert torch.equal(lse.view(torch.int32), first[1].view(torch.int32)), rep
+
+
+def test_ragged_causal_prefill_fp8():
+    say("workload ragged_causal_prefill_fp8")
+    w = W.named("ragged_causal_prefill_fp8")
+    o, lse, info = run_gpu(w)
+    say("plan", info)
+    assert info["kernel"] == 2
+    ro, rl = oracle_of(w)
+    compare(w, o, lse, ro, rl, "ragged_causal_prefill_fp8")
