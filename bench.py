@@ -69,13 +69,27 @@ def recorded_traffic(workload):
     return rec.get("traffic_bytes")
 
 
-def roofline(work, ms, traffic, mfma):
+def recorded_mfma_busy(workload):
+    """Fraction of SIMD cycles the matrix cores were busy, from the committed counter
+    record of this workload (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE), or None
+    when the record is missing or was taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_mfma_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("mfma_busy")
+
+
+def roofline(work, ms, traffic, mfma, mfma_busy=None):
     """Roofline entry of one workload: decode bodies are bound by HBM bytes, MFMA
-    tile bodies by bf16 matrix throughput."""
+    tile bodies by bf16 matrix throughput (with the counters' MFMA-busy fraction)."""
     if mfma:
         achieved = work["flops"] / (ms * 1e-3) / 1e12
         return dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), traffic=traffic)
+                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), traffic=traffic, mfma_busy=mfma_busy)
     achieved = work["bytes"] / (ms * 1e-3) / 1e9
     return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic)
@@ -220,7 +234,8 @@ def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
     out["mfma_frac"] = tfl / BF16_MFMA_PEAK_TFLOPS
     # prefill is bound by the matrix cores; decode and the shared-prefix batch
     # (whose prefix is read once for all branches) by HBM
-    out["roofline"] = roofline(work, med, recorded_traffic(name), mfma=name in MFMA_BOUND)
+    out["roofline"] = roofline(work, med, recorded_traffic(name), mfma=name in MFMA_BOUND,
+                               mfma_busy=recorded_mfma_busy(name))
     if graph:
         try:
             s = torch.cuda.Stream()
