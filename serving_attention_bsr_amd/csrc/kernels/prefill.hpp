@@ -170,32 +170,71 @@ struct MfmaBody {
 
   // ---- pieces of one tile step -------------------------------------------------
 
-  // S^T = K Q^T for the tile whose K rows start at lk (32-key blocks kb).
-  // hook(h) runs after each half of each block's products (h = 0 .. 2 KB - 1): the
-  // next tile's gather is issued there, a slice at a time, so that its loads
-  // enter the address unit's queue between products instead of in one burst.
+  // S^T = K Q^T for the tile whose K rows start at lk (32-key blocks kb).  bf16:
+  // a two-stage pipeline over groups of two k-steps: the K operands of group g + 1
+  // (both k-steps, every block) are read from LDS, then the products of group g
+  // issue with the block chains alternating, so each product's operand was read a
+  // whole group earlier and no product waits on the one just before it.  FP8: the
+  // operands are converted after their reads, and the plain order (one block
+  // after the other, each read next to its product) measured faster.
+  // hook(h) runs DK / 2 times per tile (bf16: between the reads and the products
+  // of group h): the next tile's gather is issued there a slice at a time, so that
+  // its loads enter the address unit's queue between products, not in one burst.
   template <typename Hook>
   static __device__ __forceinline__ void qk(const uint16_t* lk, const bf16x8_t (&qreg)[DK], int col, int half,
                                             f32x16_t (&s)[KB], Hook&& hook) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+    if constexpr (KV8) {
+      const uint8_t* lkb = reinterpret_cast<const uint8_t*>(lk);
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        const int r = 32 * kb + col;   // swz_k(r) == swz_k(col): 32 rows apart
-        bf16x8_t a;
-        if constexpr (KV8) {
-          // elements 16 ks + 8 half .. + 7 of the row: 8 bytes of chunk ks
-          const uint8_t* lkb = reinterpret_cast<const uint8_t*>(lk);
-          a = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(lkb + r * RB + 16 * (ks ^ swz_k(col)) + 8 * half));
-        } else {
-          a = __builtin_bit_cast(bf16x8_t,
-                                 *reinterpret_cast<const u32x4_t*>(lk + r * D + 8 * ((2 * ks + half) ^ swz_k(col))));
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+          // elements 16 ks + 8 half .. + 7 of row 32 kb + col: 8 bytes of chunk ks
+          // (swz_k(32 kb + col) == swz_k(col): 32 rows apart)
+          const bf16x8_t a = fp8x8_to_bf16x8(
+              *reinterpret_cast<const uint2*>(lkb + (32 * kb + col) * RB + 16 * (ks ^ swz_k(col)) + 8 * half));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
+          if ((ks + 1) % (DK / 2) == 0 && kb * 2 + (ks + 1) / (DK / 2) - 1 < DK / 2)
+            hook(2 * kb + (ks + 1) / (DK / 2) - 1);
         }
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
-        if ((ks + 1) % (DK / 2) == 0) hook(2 * kb + (ks + 1) / (DK / 2) - 1);
       }
+      return;
+    }
+    constexpr int G = DK / 2;
+    auto read = [&](int ks, int kb) -> bf16x8_t {
+      const int r = 32 * kb + col;  // swz_k(r) == swz_k(col): 32 rows apart
+      return __builtin_bit_cast(bf16x8_t,
+                                *reinterpret_cast<const u32x4_t*>(lk + r * D + 8 * ((2 * ks + half) ^ swz_k(col))));
+    };
+    bf16x8_t a[2][2][KB];  // [stage][k-step of the group][block]
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) a[0][j][kb] = read(j, kb);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int cur = g & 1;
+      if (g + 1 < G) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) a[cur ^ 1][j][kb] = read(2 * (g + 1) + j, kb);
+      }
+      hook(g);
+      // The order above and below is kept as written: left to itself the machine
+      // scheduler sinks every read next to its product and runs the block chains
+      // one after the other, so each product waits out a whole LDS round trip.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][j][kb], qreg[2 * g + j], s[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -417,7 +456,7 @@ struct MfmaBody {
       const bool more = t + 1 < ntiles;
       f32x16_t s[KB];
       qk(lk, qreg, col, half, s, [&](int h) {
-        constexpr int H = 2 * KB;
+        constexpr int H = DK / 2;  // hook calls per tile
         if (more) gather(krs, vrs, rpp, rows, nb, wave, lane, h * NI / H, (h + 1) * NI / H);
       });
       if (t + 2 < ntiles) load_rows(p, irs, it, t + 2, wave, lane, rows);

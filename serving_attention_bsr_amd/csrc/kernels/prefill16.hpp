@@ -30,6 +30,11 @@
 
 #include "common.hpp"
 
+// k-steps per group of the S^T pipeline
+#ifndef BSR_QK16_J
+#define BSR_QK16_J 2
+#endif
+
 namespace bsr {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -114,20 +119,44 @@ struct MfmaBody16 {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const_cast<uint16_t*>(addr)));
   }
 
-  // S^T = K Q^T: block kb covers keys 16 kb .. 16 kb + 15.
+  // S^T = K Q^T: block kb covers keys 16 kb .. 16 kb + 15.  A two-stage pipeline
+  // over groups of QK_J k-steps, as in MfmaBody::qk: the K operands of group g + 1
+  // are read from LDS, then the products of group g issue with the block chains
+  // alternating; scheduling barriers keep that order (left to itself the scheduler
+  // sinks each read next to its product, one LDS round trip per product).
+  static constexpr int QK_J = BSR_QK16_J;
+  static_assert(DK % QK_J == 0, "whole groups of k-steps");
   static __device__ __forceinline__ void qk(const uint16_t* lk, const bf16x8_t (&qreg)[DK], int r16, int grp,
                                             f32x4_t (&s)[KB]) {
+    constexpr int G = DK / QK_J;
+    auto read = [&](int ks, int kb) -> bf16x8_t {
+      // row 16 kb + r16, chunk 4 ks + grp (swz_k(16 kb + r16) == swz_k(r16))
+      return __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(lk + (16 * kb + r16) * D + 8 * ((4 * ks + grp) ^ swz_k(r16))));
+    };
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8_t a[2][QK_J][KB];  // [stage][k-step of the group][block]
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        // row 16 kb + r16, chunk 4 ks + grp (swz_k(16 kb + r16) == swz_k(r16))
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t,
-            *reinterpret_cast<const u32x4_t*>(lk + (16 * kb + r16) * D + 8 * ((4 * ks + grp) ^ swz_k(r16))));
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], s[kb], 0, 0, 0);
+    for (int j = 0; j < QK_J; ++j)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) a[0][j][kb] = read(j, kb);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int cur = g & 1;
+      if (g + 1 < G) {
+#pragma unroll
+        for (int j = 0; j < QK_J; ++j)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) a[cur ^ 1][j][kb] = read(QK_J * (g + 1) + j, kb);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < QK_J; ++j)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[cur][j][kb], qreg[QK_J * g + j], s[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
