@@ -44,6 +44,9 @@ QUEST = {"quest_sparse_decode": 64}  # page budget
 APPEND = {"append_kv_prefill": "ragged_causal_prefill"}
 
 
+STATIC_QUEUES = False  # set by --static-queues
+
+
 def kernel_source_hash():
     """sha256 over the library's kernel and host sources, in path order."""
     h = hashlib.sha256()
@@ -189,6 +192,7 @@ def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
         w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, dtype=w.dtype, causal=w.causal,
         logits_soft_cap=w.cap, max_batch=max_batch, max_total_qo=int(w.qo_indptr[-1]),
         max_total_kv=int(w.kv_lens.sum()), device=0, num_workgroups=nwg, sliding_window=w.window,
+        static_queues=STATIC_QUEUES,
     )
     work = algorithmic_work(w, composable)
     out = dict(workload=name, dtype=w.dtype, bytes=work["bytes"], flops=work["flops"])
@@ -426,9 +430,13 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--num-workgroups", type=int, default=0, help="persistent grid (0: device resident count)")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
+    ap.add_argument("--static-queues", action="store_true",
+                    help="run every work item on the workgroup the plan assigns (no run-time claiming)")
     ap.add_argument("--no-headline", action="store_true",
                     help="run only --workloads (for profiling one kernel); prints their results only")
     args = ap.parse_args()
+    global STATIC_QUEUES
+    STATIC_QUEUES = args.static_queues
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)

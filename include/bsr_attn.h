@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define BSR_ATTN_ABI_VERSION 3
+#define BSR_ATTN_ABI_VERSION 4
 
 typedef enum bsr_status {
   BSR_OK = 0,
@@ -127,7 +127,15 @@ typedef struct bsr_attn_config {
                               the window of W keys described above; bsr_attn_plan only
                               (bsr_attn_plan_composable rejects it).  The planner gives
                               each query tile only the keys its window can reach */
-  int32_t reserved;        /* must be 0 */
+  int32_t static_queues;   /* 0 (default): in plans for the MFMA tile kernel, the tail
+                              of each workgroup's queue (items starting after 3/4 of its
+                              planned load) is claimed at run time, one item at a time,
+                              longest first, from a counter in the workspace, by
+                              whichever workgroup is free, so that faster CUs (the chip's
+                              XCDs run at measurably different rates) take more of it.
+                              1: every item runs on the workgroup the plan assigns.  The
+                              items, partial states and merges are the same either way,
+                              so results are bitwise identical between the two */
   const float* alibi_slopes; /* NULL: no ALiBi.  Otherwise host array [num_qo_heads],
                               read at create: query head h adds m_h * (j - p) to the
                               scaled logit of key j before the soft-cap, p being the

@@ -100,7 +100,7 @@ int validate_config(const bsr_attn_config* c) {
   if (c->cost_mfma > 16 * 256) return fail(BSR_ERR_INVALID_ARG, "cost_mfma too large");
   if (c->slot2_speed > 64) return fail(BSR_ERR_INVALID_ARG, "slot2_speed too large");
   if (c->sliding_window < 0) return fail(BSR_ERR_INVALID_ARG, "sliding_window must be >= 0");
-  if (c->reserved != 0) return fail(BSR_ERR_INVALID_ARG, "reserved must be 0");
+  if (c->static_queues != 0 && c->static_queues != 1) return fail(BSR_ERR_INVALID_ARG, "static_queues must be 0 or 1");
   if (c->alibi_slopes != nullptr)
     for (int32_t hq = 0; hq < c->num_qo_heads; ++hq)
       if (!std::isfinite(c->alibi_slopes[hq])) return fail(BSR_ERR_INVALID_ARG, "ALiBi slopes must be finite");
@@ -219,6 +219,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   pc.bf16 = bf16;
   pc.cap = cap;
   pc.kv8 = kv8;
+  pc.static_queues = cfg->static_queues != 0;
   std::memcpy(pc.num_wg, h->num_wg, sizeof(pc.num_wg));
   pc.alpha = cfg->cost_alpha > 0 ? cfg->cost_alpha : 1;
   pc.beta = cfg->cost_beta > 0 ? cfg->cost_beta : 1;
@@ -257,7 +258,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
   const int64_t max_tasks = int64_t(cfg->max_total_qo) * hk;
   const int64_t max_srcs = 2 * max_tasks + 2LL * max_wg * tile_max;
   // (+ ALiBi slopes and one tree-mask row per query token)
-  int64_t cap_bytes = sizeof(bsr::PlanHeader) + 16 + 4LL * max_wg + 4 * max_items +
+  int64_t cap_bytes = sizeof(bsr::PlanHeader) + 16 + 16 + 4LL * max_wg + 4 * max_items +
                       2 * 4LL * (max_wg + 1) + int64_t(sizeof(bsr::WorkItem)) * max_items +
                       int64_t(sizeof(bsr::MergeTask)) * max_tasks +
                       int64_t(sizeof(bsr::MergeSrc)) * max_srcs + 4LL * cfg->num_qo_heads +

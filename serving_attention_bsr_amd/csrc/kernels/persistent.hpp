@@ -93,7 +93,8 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   // the whole header in one read (its fields are uniform; the empty asm keeps the
   // offsets from being loaded separately after the check below)
   const PlanHeader h = *plan_header(ws);
-  asm volatile("" ::"s"(h.off_epochs), "s"(h.off_item_ptr), "s"(h.off_items), "s"(h.off_flags));
+  asm volatile("" ::"s"(h.off_epochs), "s"(h.off_item_ptr), "s"(h.off_items), "s"(h.off_flags), "s"(h.pool_begin),
+               "s"(h.off_claim));
   const Variant var{h.off_alibi != 0, reinterpret_cast<const float*>(ws + h.off_alibi),
                     reinterpret_cast<const uint64_t*>(ws + h.off_tree)};
   const PlanHeader* hdr = &h;
@@ -116,6 +117,13 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   // is issued here and waited for there, off the items' latency chain
   const int32_t epoch = epochs[wg] + 1;
   const int g = p.group;
+  // claim counters: this run uses the one of its epoch's parity (cleared by the
+  // previous run, or zero as uploaded) and clears the other for the next run; the
+  // previous run, the last user of that one, has ended before this one started
+  const bool pooled = hdr->pool_begin < hdr->num_items;
+  int32_t* claims = plan_i32(ws, hdr->off_claim);
+  if (pooled && wg == 0 && threadIdx.x == 0)
+    __hip_atomic_store(claims + ((epoch + 1) & 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- attention items -------------------------------------------------------
   // The queue is read-only during the run: scalar loads, and the next item is
@@ -126,11 +134,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   bool any_partial = false;
   WorkItem nxt;
   if (ib < ie) nxt = load_invariant(items + ib);
-  for (int32_t i = ib; i < ie; ++i) {
-    if (i == ib + 1) BSR_STAMP(6);  // (timeline builds: after the first and second items)
-    if (i == ib + 2) BSR_STAMP(7);
-    const WorkItem it = nxt;
-    if (i + 1 < ie) nxt = load_invariant(items + i + 1);
+  auto process = [&](const WorkItem& it) {
     if (it.flags & kItemPartial) {
       float* po = reinterpret_cast<float*>(ws + p.partial_o_off);
       float* pl = reinterpret_cast<float*>(ws + p.partial_lse_off);
@@ -158,28 +162,80 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
       };
       K::attend(p, it, var, lds, emit);
     }
-  }
-
-  BSR_STAMP(1);
-  // Stamps for the partial states this workgroup wrote: every wavefront waits
-  // until its device-scope stores have completed (vector memory counter at 0),
-  // the workgroup meets, and wavefront 0 stores the stamps.  This is the
-  // agent-scope release sequence of the AMDGPU memory model (wait for the vector
-  // memory counter, then store the flag) without its write-back of the L2 cache,
-  // which only data written into the L2 by non-atomic stores needs: every store of
-  // a partial state above must stay an agent-scope atomic store, and the merge's
-  // reads agent-scope atomic loads (the acquire side without the L2 invalidate).
-  if (any_partial) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      for (int32_t i = ib + static_cast<int32_t>(threadIdx.x); i < ie; i += 64) {
-        const WorkItem& it = items[i];
-        if (it.flags & kItemPartial)
-          __hip_atomic_store(flags + it.flag_id, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // The workgroup's queue first, then the claimed pool (see below): one loop, so
+  // that the bodies are inlined once.
+  __shared__ int32_t next_claim;
+  int32_t* claim = claims + (epoch & 1);
+  int32_t qi = ib;        // next queued item
+  bool in_pool = false;   // the queue is done
+  bool part_prev = false; // the previous pool item wrote a partial state
+  int32_t flag_prev = 0;
+  int32_t after = 0;      // thread 0: the claim issued for the next pool item
+  while (true) {
+    int32_t i;
+    if (qi < ie) {
+      i = qi++;
+    } else {
+      if (!in_pool) {
+        BSR_STAMP(6);  // (timeline builds: the queue is done)
+        // Stamps for the partial states of the queue: every wavefront waits until
+        // its device-scope stores have completed (vector memory counter at 0), the
+        // workgroup meets, and wavefront 0 stores the stamps.  This is the
+        // agent-scope release sequence of the AMDGPU memory model (wait for the
+        // vector memory counter, then store the flag) without its write-back of the
+        // L2 cache, which only data written into the L2 by non-atomic stores needs:
+        // every store of a partial state must stay an agent-scope atomic store, and
+        // the merge's reads agent-scope atomic loads (the acquire side without the
+        // L2 invalidate).
+        if (any_partial) {
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+          __syncthreads();
+          if (threadIdx.x < 64) {
+            for (int32_t k = ib + static_cast<int32_t>(threadIdx.x); k < ie; k += 64) {
+              const WorkItem& it = items[k];
+              if (it.flags & kItemPartial)
+                __hip_atomic_store(flags + it.flag_id, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+        if (!pooled) break;
+        // Claimed items: the pool runs in array order (the plan's longest-first
+        // order), one item per claim; the next claim is issued before an item runs
+        // and read after it.  A partial state is stamped right after its item, with
+        // the same release sequence.  Every pool item is claimed by a workgroup that
+        // runs it to the end without waiting on anything, and a workgroup reaches
+        // its merge tasks only after the pool is exhausted, so every stamp a merge
+        // waits for is stored.
+        in_pool = true;
+        if (threadIdx.x == 0)
+          next_claim = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+      } else {
+        if (part_prev) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();  // every partial store done; every wavefront past next_claim
+        if (threadIdx.x == 0) {
+          if (part_prev) __hip_atomic_store(flags + flag_prev, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          next_claim = after;
+        }
+        __syncthreads();
       }
+      i = __builtin_amdgcn_readfirstlane(hdr->pool_begin + next_claim);
+      if (i >= hdr->num_items) break;
+      nxt = load_invariant(items + i);
+      if (threadIdx.x == 0) after = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    const WorkItem it = nxt;
+    // the next queued item is read while this one runs
+    if (qi < ie) nxt = load_invariant(items + qi);
+    part_prev = (it.flags & kItemPartial) != 0;
+    flag_prev = it.flag_id;
+    process(it);
+#ifdef BSR_TRACE
+    if (in_pool && threadIdx.x == 0) reinterpret_cast<uint64_t*>(ws + p.trace_off)[wg * 8 + 7] += 1;  // claimed items
+#endif
   }
+  BSR_STAMP(1);
 
   BSR_STAMP(2);
   // ---- contraction of partial states -----------------------------------------

@@ -99,7 +99,7 @@ struct MergeSrc {  // 8 bytes
   int32_t flag_id;      // ready flag of the item that wrote it
 };
 
-struct PlanHeader {  // 80 bytes
+struct PlanHeader {  // 88 bytes
   int32_t magic;
   int32_t kernel;
   int32_t num_wg;
@@ -120,11 +120,17 @@ struct PlanHeader {  // 80 bytes
   int32_t spin_limit;  // polls before a merge gives up on a ready stamp
   int32_t off_alibi;   // float [H_qo] ALiBi slopes / sm_scale, or 0 without ALiBi
   int32_t off_tree;    // uint64 [total_qo] tree-mask rows, or 0 without tree masks
+  // Items pool_begin .. num_items - 1 are claimed at run time, in array order, by
+  // whichever workgroup is free (items 0 .. pool_begin - 1 are the per-workgroup
+  // queues); off_claim holds two int32 claim counters, used by alternate runs
+  // (epoch parity), each run clearing the other one for the next.
+  int32_t pool_begin;
+  int32_t off_claim;
 };
 
 static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
 static_assert(sizeof(MergeTask) == 16, "MergeTask layout");
 static_assert(sizeof(MergeSrc) == 8, "MergeSrc layout");
-static_assert(sizeof(PlanHeader) == 80, "PlanHeader layout");
+static_assert(sizeof(PlanHeader) == 88, "PlanHeader layout");
 
 }  // namespace bsr

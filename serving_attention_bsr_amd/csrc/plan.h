@@ -34,6 +34,8 @@ struct PlanConfig {
   bool kv8 = false;  // K/V are FP8 codes: decode body only (no MFMA tiles)
   int32_t slot2_speed16 = 16;
   int32_t window = 0;  // sliding window in keys (0: none)
+  // every item on the workgroup it is assigned to (no run-time claiming)
+  bool static_queues = false;
   // ALiBi: per query head, slope / sm_scale (empty: no ALiBi)
   std::vector<float> alibi_raw;
   // capacities (plan rejected beyond them)
@@ -66,6 +68,12 @@ struct PlanResult {
 constexpr int kMaxDecodeRows = 8;
 // KV granularity that chunk lengths are rounded to (tokens).
 constexpr int kChunkGranule = 64;
+// Share of each workgroup's planned load, in sixteenths, whose items are claimed
+// at run time instead of queued (the tail of the queue).
+#ifndef BSR_POOL_TAIL16
+#define BSR_POOL_TAIL16 4
+#endif
+constexpr int kPoolTail16 = BSR_POOL_TAIL16;
 // The planner also tries L_kv / k for k up to this and keeps the smallest
 // predicted makespan (the pages' L_kv unless another is clearly better).
 constexpr int kChunkCandidates = 4;

@@ -81,7 +81,7 @@ class bsr_attn_config(ctypes.Structure):
         ("cost_mfma", ctypes.c_int32),
         ("slot2_speed", ctypes.c_int32),
         ("sliding_window", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("static_queues", ctypes.c_int32),
         ("alibi_slopes", ctypes.POINTER(ctypes.c_float)),
     ]
 
@@ -118,7 +118,7 @@ class bsr_plan_info(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 3  # BSR_ATTN_ABI_VERSION of the struct layouts above
+ABI_VERSION = 4  # BSR_ATTN_ABI_VERSION of the struct layouts above
 
 
 def load():
@@ -335,6 +335,7 @@ class BsrAttention:
         slot2_speed: int = 0,
         sliding_window: int = 0,
         alibi_slopes=None,
+        static_queues: bool = False,
     ):
         cfg = bsr_attn_config()
         cfg.num_qo_heads = num_qo_heads
@@ -357,6 +358,7 @@ class BsrAttention:
         cfg.cost_mfma = cost_mfma
         cfg.slot2_speed = slot2_speed
         cfg.sliding_window = sliding_window
+        cfg.static_queues = int(static_queues)
         if alibi_slopes is not None:
             slopes = np.ascontiguousarray(np.asarray(alibi_slopes, dtype=np.float32))
             if slopes.shape != (num_qo_heads,):

@@ -1,8 +1,10 @@
 """Decoder of the plan bytes a host-only handle stages, and a CPU float64 executor.
 
 The layout decoded here is the one documented in the library's layout header:
-an 80-byte header of int32 counts, offsets, the kernel instance and the wait bound, then status words, per-workgroup epochs,
-ready flags, per-workgroup item queues (CSR), 64-byte work items, per-workgroup
+an 88-byte header of int32 counts, offsets, the kernel instance, the wait bound and the
+first claimed item, then status words, claim counters, per-workgroup epochs, ready
+flags, per-workgroup item queues (CSR), 64-byte work items (the queues' items, then
+the pool that workgroups claim at run time), per-workgroup
 merge queues (CSR), 16-byte merge tasks and 8-byte merge sources.
 
 The executor runs the plan's work items and merge map with the oracle's
@@ -19,7 +21,8 @@ import oracle
 HEADER_FIELDS = [
     "magic", "kernel", "num_wg", "num_items", "num_merge", "num_srcs", "num_flags",
     "off_status", "off_epochs", "off_flags", "off_item_ptr", "off_items", "off_merge_ptr",
-    "off_merge", "off_srcs", "blob_bytes", "instance", "spin_limit", "off_alibi", "off_tree",
+    "off_merge", "off_srcs", "blob_bytes", "instance", "spin_limit", "off_alibi", "off_tree", "pool_begin",
+    "off_claim",
 ]
 HEADER_BYTES = 4 * len(HEADER_FIELDS)
 ITEM = np.dtype([
@@ -45,6 +48,7 @@ def decode(blob: np.ndarray) -> dict:
     def arr(off, dtype, n):
         return np.frombuffer(blob[off : off + np.dtype(dtype).itemsize * n].tobytes(), dtype=dtype)
 
+    assert 0 <= hdr["pool_begin"] <= hdr["num_items"]
     tree = None
     if hdr["off_tree"]:
         end = hdr["off_tree"] + 8 * ((hdr["blob_bytes"] - hdr["off_tree"]) // 8)
@@ -55,6 +59,7 @@ def decode(blob: np.ndarray) -> dict:
         epochs=arr(hdr["off_epochs"], "<i4", nwg),
         flags=arr(hdr["off_flags"], "<i4", hdr["num_flags"]),
         item_ptr=arr(hdr["off_item_ptr"], "<i4", nwg + 1),
+        claims=arr(hdr["off_claim"], "<i4", 2),
         items=arr(hdr["off_items"], ITEM, hdr["num_items"]),
         merge_ptr=arr(hdr["off_merge_ptr"], "<i4", nwg + 1),
         merge=arr(hdr["off_merge"], TASK, hdr["num_merge"]),
@@ -73,39 +78,40 @@ def execute(plan, q, k_pool, v_pool, kv_indices, group, page_size, scale, cap, a
     partial = {}
     written = np.zeros((total, h_qo), dtype=np.int64)
     nwg = plan["header"]["num_wg"]
-    for w in range(nwg):
-        for it in plan["items"][plan["item_ptr"][w] : plan["item_ptr"][w + 1]]:
-            kb, ke = int(it["kv_begin"]), int(it["kv_end"])
-            tau = np.arange(kb, ke)
-            pages = kv_indices[int(it["page_begin"]) + tau // page_size]
-            k = np.asarray(k_pool[pages, int(it["kv_head"]), tau % page_size, :], dtype=np.float64)
-            v = np.asarray(v_pool[pages, int(it["kv_head"]), tau % page_size, :], dtype=np.float64)
-            for t in range(int(it["qo_count"])):
-                token = int(it["qo_begin"]) + t
-                limit = int(it["causal_limit"]) + t
-                vis = (tau <= limit) & (tau >= int(it["window_lo"]) + t)
-                tlo = int(it["tree_lo"])
-                if tlo != NO_TREE:
-                    row = np.uint64(plan["tree"][token])
-                    bit = np.clip(tau - tlo, 0, 63).astype(np.uint64)
-                    vis &= (tau < tlo) | (((row >> bit) & np.uint64(1)) == 1)
-                for j in range(group):
-                    head = int(it["kv_head"]) * group + j
-                    bias = None
-                    if alibi_slopes is not None:
-                        bias = (float(alibi_slopes[head]) * (tau[vis] - (int(it["q_pos"]) + t)))[None, :]
-                    o1, l1 = oracle.attention_dense(
-                        np.asarray(q[token : token + 1, head, :], dtype=np.float64), k[vis], v[vis], scale, cap,
-                        bias=bias,
-                    )
-                    if it["flags"] & ITEM_PARTIAL:
-                        row = int(it["partial_row"]) + t * group + j
-                        assert row not in partial, "partial row written twice"
-                        partial[row] = (o1[0], l1[0], int(it["flag_id"]))
-                    else:
-                        out[token, head] = o1[0]
-                        lse[token, head] = l1[0]
-                        written[token, head] += 1
+    # every item once: the per-workgroup queues, then the claimed pool (which
+    # workgroup runs an item does not change its result)
+    for it in plan["items"]:
+        kb, ke = int(it["kv_begin"]), int(it["kv_end"])
+        tau = np.arange(kb, ke)
+        pages = kv_indices[int(it["page_begin"]) + tau // page_size]
+        k = np.asarray(k_pool[pages, int(it["kv_head"]), tau % page_size, :], dtype=np.float64)
+        v = np.asarray(v_pool[pages, int(it["kv_head"]), tau % page_size, :], dtype=np.float64)
+        for t in range(int(it["qo_count"])):
+            token = int(it["qo_begin"]) + t
+            limit = int(it["causal_limit"]) + t
+            vis = (tau <= limit) & (tau >= int(it["window_lo"]) + t)
+            tlo = int(it["tree_lo"])
+            if tlo != NO_TREE:
+                row = np.uint64(plan["tree"][token])
+                bit = np.clip(tau - tlo, 0, 63).astype(np.uint64)
+                vis &= (tau < tlo) | (((row >> bit) & np.uint64(1)) == 1)
+            for j in range(group):
+                head = int(it["kv_head"]) * group + j
+                bias = None
+                if alibi_slopes is not None:
+                    bias = (float(alibi_slopes[head]) * (tau[vis] - (int(it["q_pos"]) + t)))[None, :]
+                o1, l1 = oracle.attention_dense(
+                    np.asarray(q[token : token + 1, head, :], dtype=np.float64), k[vis], v[vis], scale, cap,
+                    bias=bias,
+                )
+                if it["flags"] & ITEM_PARTIAL:
+                    row = int(it["partial_row"]) + t * group + j
+                    assert row not in partial, "partial row written twice"
+                    partial[row] = (o1[0], l1[0], int(it["flag_id"]))
+                else:
+                    out[token, head] = o1[0]
+                    lse[token, head] = l1[0]
+                    written[token, head] += 1
     for w in range(nwg):
         for m in plan["merge"][plan["merge_ptr"][w] : plan["merge_ptr"][w + 1]]:
             srcs = plan["srcs"][int(m["src_begin"]) : int(m["src_begin"]) + int(m["src_count"])]

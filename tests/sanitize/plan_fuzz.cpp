@@ -60,6 +60,7 @@ int main(int argc, char** argv) {
     }
     cfg.cus = pick(0, 1) ? nwg / 2 : 0;
     cfg.slot2_speed16 = pick(8, 16);
+    cfg.static_queues = pick(0, 1) == 1;
     cfg.mfma_w16 = pick(16, 400);
     cfg.gamma = pick(0, 1024);
     cfg.min_chunk = 64 * pick(1, 4);
@@ -133,16 +134,31 @@ int main(int argc, char** argv) {
     CHECK(h.magic == kPlanMagic && h.blob_bytes == n);
     CHECK(h.num_wg > 0 && h.num_wg <= nwg);
     CHECK(h.spin_limit > 0);
-    const int32_t offs[] = {h.off_status, h.off_epochs, h.off_flags, h.off_item_ptr,
+    const int32_t offs[] = {h.off_status, h.off_claim, h.off_epochs, h.off_flags, h.off_item_ptr,
                             h.off_items, h.off_merge_ptr, h.off_merge, h.off_srcs};
     for (int32_t o : offs) CHECK(o >= static_cast<int32_t>(sizeof(PlanHeader)) && o <= n && o % 16 == 0);
+    CHECK(h.off_claim + 8 <= n);
+    {
+      int32_t claim[2];
+      std::memcpy(claim, res.blob.data() + h.off_claim, sizeof(claim));
+      CHECK(claim[0] == 0 && claim[1] == 0);
+    }
     CHECK(h.off_items + int64_t(h.num_items) * int64_t(sizeof(WorkItem)) <= n);
     CHECK(h.off_srcs + int64_t(h.num_srcs) * int64_t(sizeof(MergeSrc)) <= n);
     const uint8_t* base = res.blob.data();
     std::vector<int32_t> iptr(h.num_wg + 1), mptr(h.num_wg + 1);
     std::memcpy(iptr.data(), base + h.off_item_ptr, 4 * (h.num_wg + 1));
     std::memcpy(mptr.data(), base + h.off_merge_ptr, 4 * (h.num_wg + 1));
-    CHECK(iptr[0] == 0 && iptr[h.num_wg] == h.num_items);
+    CHECK(h.pool_begin >= 0 && h.pool_begin <= h.num_items);
+    CHECK(iptr[0] == 0 && iptr[h.num_wg] == h.pool_begin);
+    CHECK(!cfg.static_queues || h.pool_begin == h.num_items);
+    // only tile-grid plans claim items; every queue keeps its first item
+    if (h.kernel != kKindMfma) CHECK(h.pool_begin == h.num_items);
+    if (h.pool_begin < h.num_items) {
+      int busy = 0;
+      for (int w = 0; w < h.num_wg; ++w) busy += iptr[w + 1] > iptr[w];
+      CHECK(busy > 0);
+    }
     CHECK(mptr[0] == 0 && mptr[h.num_wg] == h.num_merge);
     for (int w = 0; w < h.num_wg; ++w) CHECK(iptr[w] <= iptr[w + 1] && mptr[w] <= mptr[w + 1]);
     std::vector<char> flag_written(h.num_flags, 0);

@@ -28,11 +28,11 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert lib.bsr_attn_abi_version() == 3
+    assert lib.bsr_attn_abi_version() == 4
 
 
 def test_struct_sizes_match_header():
-    # bsr_attn_config: 8 int32/float, max_batch, max_total_qo, int64, 9 int32, reserved,
+    # bsr_attn_config: 8 int32/float, max_batch, max_total_qo, int64, 9 int32, static_queues,
     # the ALiBi slope pointer
     assert lib.ctypes.sizeof(lib.bsr_attn_config) == 96
     assert lib.ctypes.sizeof(lib.bsr_plan_info) == 64

@@ -14,6 +14,9 @@ kernels (needs an MI355X).
   the host: a stamp no item writes and a small wait bound in the uploaded plan)
   ends normally and check() reports it.
 * A plan made without a workspace leaves the uploaded plan in force.
+* Items claimed at run time and items on their planned workgroups give the same
+  bits (the named parity tests check the claimed layout, the default, against
+  the oracle).
 """
 
 import numpy as np
@@ -270,3 +273,38 @@ def test_plan_without_workspace_keeps_the_uploaded_plan():
     torch.cuda.synchronize()
     h.check()
     assert torch.equal(_bits(o), o1) and torch.equal(_bits(l), l1)
+
+
+def _outputs(w, composable, **kw):
+    h = handle_for(w, **kw)
+    q, k, v, idx = to_gpu(w)
+    if composable:
+        info = h.plan_composable([f.as_dict() for f in w.formats], w.batch)
+        idx = torch.from_numpy(np.ascontiguousarray(w.kv_indices_formats)).to(q.device)
+    else:
+        info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
+    o, lse = h.run(q, k, v, idx)
+    torch.cuda.synchronize()
+    h.check()
+    return info, _bits(o), _bits(lse)
+
+
+@pytest.mark.parametrize("name, nwg", [("split_prefill", 64), ("ragged_causal_prefill", 0)])
+def test_claimed_items_match_the_static_queues_bitwise(name, nwg):
+    """Work items claimed at run time (the default on the MFMA tile grid) and every
+    item on the workgroup the plan names give the same bits: the items, partial
+    states and merge order are the same; only which workgroup runs an item
+    differs.  (The split prefill on 64 workgroups has long queues and merges.)"""
+    say("claimed vs static queues", name, nwg)
+    if name == "split_prefill":
+        w = W.build("split_prefill", 48, [300, 64, 1000], [700, 9000, 1500], 1, 32, 8, 128, dtype="bf16",
+                    causal=True)
+    else:
+        w = W.named(name)
+    info_d, o_d, l_d = _outputs(w, False, num_workgroups=nwg)
+    info_s, o_s, l_s = _outputs(w, False, num_workgroups=nwg, static_queues=True)
+    say("plans", info_d["num_items"], info_d["num_partial_items"], info_s["num_items"])
+    assert info_d["kernel"] == lib.KERNEL_MFMA and info_d["num_items"] == info_s["num_items"]
+    if name == "split_prefill":
+        assert info_d["num_partial_items"] > 0
+    assert torch.equal(o_d, o_s) and torch.equal(l_d, l_s)

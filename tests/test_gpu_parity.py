@@ -199,7 +199,7 @@ def test_two_per_cu_plan_is_balanced_in_time():
     w = W.named("ragged_causal_prefill", tensors=False)
     h = lib.BsrAttention(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, dtype=w.dtype, causal=w.causal,
                          max_batch=w.batch, max_total_qo=int(w.qo_indptr[-1]), max_total_kv=int(w.kv_lens.sum()),
-                         device=0)
+                         device=0, static_queues=True)
     info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     say("plan", info, "cus", cus)

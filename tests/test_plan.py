@@ -111,7 +111,7 @@ def test_mixed_grid_weights_mfma_tokens():
 
     def plan(cost_mfma):
         h = host_handle(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, nwg=256, max_batch=mb,
-                        cost_mfma=cost_mfma)
+                        cost_mfma=cost_mfma, static_queues=True)
         info = h.plan_composable(fm, w.batch)
         return info, plan_blob.decode(h.plan_bytes())
 
@@ -150,10 +150,13 @@ def unit_chunks(plan, group):
 @pytest.mark.parametrize("nwg", [1, 64, 512])
 def test_named_workload_plan_invariants(name, nwg):
     w = W.named(name, tensors=False)
-    h = host_handle(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype, w.causal, w.cap, nwg)
+    # (the plan's own assignment: every item on the workgroup it is given)
+    h = host_handle(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype, w.causal, w.cap, nwg,
+                    static_queues=True)
     info = h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
     plan = plan_blob.decode(h.plan_bytes())
     items = plan["items"]
+    assert plan["header"]["pool_begin"] == len(items)
     lens = items["kv_end"] - items["kv_begin"]
     # chunks never exceed L_kv
     assert np.all(lens <= info["kv_chunk"])
@@ -221,7 +224,8 @@ def test_named_workload_plan_invariants(name, nwg):
     first = h.plan_bytes()
     h.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
     assert np.array_equal(first, h.plan_bytes())
-    h2 = host_handle(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype, w.causal, w.cap, nwg)
+    h2 = host_handle(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype, w.causal, w.cap, nwg,
+                     static_queues=True)
     h2.plan(w.qo_indptr, w.kv_indptr, w.last_page_len)
     assert np.array_equal(first, h2.plan_bytes())
 
