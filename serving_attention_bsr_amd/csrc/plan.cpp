@@ -578,6 +578,18 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   const int64_t min_chunk = round_up(std::max(cfg.min_chunk, 1), kChunkGranule);
   const int64_t base_chunk =
       std::max<int64_t>(round_up(std::max<int64_t>(ceil_div(total_kv, nwg), 1), kChunkGranule), min_chunk);
+  // A lower bound on every candidate's makespan: each candidate's loads sum to at
+  // least the units' unsplit costs (cutting adds the fixed item cost, merges add
+  // theirs), and the busiest workgroup finishes no earlier than that sum spread
+  // over all workgroups at their speeds.  A candidate replaces the best only if it
+  // is 3 % shorter, so once the best is within 3 % of the bound no later candidate
+  // can: the remaining ones are not scored (the plan is the same).
+  int64_t lb_total = 0, sum_speed16 = 0;
+  for (const Unit& u : units)
+    if (!(composable && u.l_eff == 0))
+      lb_total += cfg.alpha * static_cast<int64_t>(u.nt) * g + cfg.beta * weighted(u, u.l_eff) + cfg.gamma;
+  for (int32_t w = 0; w < nwg; ++w) sum_speed16 += speed16[w];
+  const int64_t lower_bound = lb_total * 16 / std::max<int64_t>(sum_speed16, 1);
   Schedule best;
   bool have = false;
   int64_t last_chunk = -1;
@@ -608,6 +620,7 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       best = std::move(cand);
       have = true;
     }
+    if (best.makespan * 97 <= lower_bound * 100) break;
   }
   assign_merges(cfg, nwg, speed16, &best);
   if (best.partial_rows > cfg.max_partial_rows) {
@@ -669,8 +682,10 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       wg_at[w] += items[i].cost;
       wg_count[w] += 1;
     }
-    std::stable_sort(pool_order.begin(), pool_order.end(),
-                     [&](int32_t a, int32_t b) { return items[a].cost > items[b].cost; });
+    // (longest-first assignments already list the pool in that order)
+    auto longer = [&](int32_t a, int32_t b) { return items[a].cost > items[b].cost; };
+    if (!std::is_sorted(pool_order.begin(), pool_order.end(), longer))
+      std::stable_sort(pool_order.begin(), pool_order.end(), longer);
   }
   hdr.pool_begin = num_static;
   int64_t off = sizeof(PlanHeader);
