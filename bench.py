@@ -252,6 +252,17 @@ def bench_workload(name, steps, warmup, flush, graph=True, nwg=0, mode="read"):
                 step()
             gt, _ = timed_steps(g.replay, steps, warmup, stream, flush, mode)
             out["graph_ms_median"] = float(np.median(gt))
+            # a graph launch has a fixed cost of its own (its start and end in the
+            # runtime); ten runs in one graph against ten eager runs, per run (one
+            # cache flush before each group of ten)
+            g10 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g10, stream=s):
+                for _ in range(10):
+                    step()
+            gt10, _ = timed_steps(g10.replay, max(steps // 4, 3), 2, stream, flush, mode)
+            et10, _ = timed_steps(lambda: [step() for _ in range(10)], max(steps // 4, 3), 2, stream, flush, mode)
+            out["graph10_ms_per_run"] = float(np.median(gt10)) / 10
+            out["eager10_ms_per_run"] = float(np.median(et10)) / 10
         except Exception as exc:  # report, do not hide
             out["graph_error"] = repr(exc)
     return out, (w, h)

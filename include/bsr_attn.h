@@ -128,7 +128,7 @@ typedef struct bsr_attn_config {
                               (bsr_attn_plan_composable rejects it).  The planner gives
                               each query tile only the keys its window can reach */
   int32_t static_queues;   /* 0 (default): in plans for the MFMA tile kernel, the tail
-                              of each workgroup's queue (items starting after 3/4 of its
+                              of each workgroup's queue (items starting after 7/8 of its
                               planned load) is claimed at run time, one item at a time,
                               longest first, from a counter in the workspace, by
                               whichever workgroup is free, so that faster CUs (the chip's
