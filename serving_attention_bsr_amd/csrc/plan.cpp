@@ -220,10 +220,15 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
     };
     std::stable_sort(short_u.begin(), short_u.end(), longer);
     std::stable_sort(long_u.begin(), long_u.end(), longer);
-    const int64_t target = ceil_div(total, nwg);
+    // each workgroup is filled to its share of the total at its speed (all equal
+    // unless the grid's workgroups run at different speeds); the heap holds
+    // (load - target, workgroup), so its top is the workgroup with the most room
+    int64_t sum_speed = 0;
+    for (int32_t w = 0; w < nwg; ++w) sum_speed += speed16[w];
+    auto target_of = [&](int32_t w) { return ceil_div(total * speed16[w], std::max<int64_t>(sum_speed, 1)); };
     using Slot = std::pair<int64_t, int32_t>;
     std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
-    for (int32_t w = 0; w < nwg; ++w) heap.push({0, w});
+    for (int32_t w = 0; w < nwg; ++w) heap.push({-target_of(w), w});
     auto place = [&](int32_t ui, int64_t b, int64_t e) {
       Slot s = heap.top();
       heap.pop();
@@ -235,7 +240,7 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
       owner.push_back(s.second);
       items.push_back({w, c, ui, 0});
       s.first += c;
-      load[s.second] = s.first;
+      load[s.second] += c;
       heap.push(s);
     };
     for (int32_t ui : short_u) place(ui, 0, units[ui].l_eff);
@@ -247,7 +252,7 @@ int schedule(const PlanConfig& cfg, const std::vector<BlockRow>& rows, const std
         const int64_t fixed = item_cost(ui, 0);
         // room left in the least-loaded workgroup, in this unit's KV tokens
         const int64_t space =
-            (target - heap.top().first - fixed) * 16 / (static_cast<int64_t>(units[ui].w16) * std::max<int64_t>(cfg.beta, 1));
+            (-heap.top().first - fixed) * 16 / (static_cast<int64_t>(units[ui].w16) * std::max<int64_t>(cfg.beta, 1));
         // pieces round up to the granule (the rounding overshoot is absorbed by
         // workgroups that end up with no long piece) and are never tiny
         const int64_t floor_piece = std::max<int64_t>(min_piece, 4 * kChunkGranule);
@@ -459,7 +464,7 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
 
   // ---- 1. kernel kind and query tile -----------------------------------------
   bool any_decode = false, any_wide = false;
-  int64_t max_decode_rows = 0, wide_rows_sum = 0, wide_count = 0;
+  int64_t max_decode_rows = 0;
   for (const BlockRow& r : rows) {
     if (r.qo_len == 0) continue;
     const int64_t fr = static_cast<int64_t>(r.qo_len) * g;
@@ -468,8 +473,6 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       max_decode_rows = std::max(max_decode_rows, fr);
     } else {
       any_wide = true;
-      wide_rows_sum += fr;
-      wide_count += 1;
     }
   }
   int32_t kernel = kKindDecode;
