@@ -465,14 +465,19 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   // ---- 1. kernel kind and query tile -----------------------------------------
   bool any_decode = false, any_wide = false;
   int64_t max_decode_rows = 0;
+  // KV tokens streamed by decode-sized rows and by tiles (once per query tile)
+  int64_t decode_kv = 0, tile_kv = 0;
+  const int64_t tile_rows = mfma_tile(cfg.head_dim);
   for (const BlockRow& r : rows) {
     if (r.qo_len == 0) continue;
     const int64_t fr = static_cast<int64_t>(r.qo_len) * g;
     if (fr <= kMaxDecodeRows) {
       any_decode = true;
       max_decode_rows = std::max(max_decode_rows, fr);
+      decode_kv += r.kv_len;
     } else {
       any_wide = true;
+      tile_kv += ceil_div(fr, tile_rows) * r.kv_len;
     }
   }
   int32_t kernel = kKindDecode;
@@ -492,7 +497,13 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       decode_rows = kMaxDecodeRows;
       q_tile = decode_rows;
     } else {
-      kernel = any_decode ? kKindMixed : kKindMfma;
+      // Decode-sized rows next to tiles: the mixed grid (decode body for them, one
+      // workgroup per CU) only when they stream at least a quarter of the KV
+      // tokens; otherwise every row runs as a tile on the two-per-CU tile grid,
+      // where a tile runs several times faster per CU than in the mixed grid's one
+      // wavefront per SIMD (tree-masked speculative decode, 8 % decode-row tokens:
+      // 457 -> 175 us; shared-prefix batch, 35 %: mixed 91 us, tiles 97 us).
+      kernel = any_decode && decode_kv * 4 >= decode_kv + tile_kv ? kKindMixed : kKindMfma;
       // the kernels implement one MFMA tile height per head dim (the smallest tile
       // at least the mean folded length, from a menu of one)
       const int32_t tile = mfma_tile(cfg.head_dim);

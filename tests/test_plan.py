@@ -231,12 +231,22 @@ def test_named_workload_plan_invariants(name, nwg):
 
 
 def test_kernel_choice_follows_query_tile_rule():
+    """Decode rows alone run on the decode body, wide rows on tiles; both together
+    on the mixed grid only when the decode-sized rows stream at least a quarter of
+    the KV tokens (tiles counted once per 128-row query tile), otherwise every row
+    runs as a tile."""
     h = host_handle(32, 8, 128, 16, nwg=16)
     assert h.plan([0, 1, 2], [0, 1, 2], [16, 16])["kernel"] == lib.KERNEL_DECODE
     assert h.plan([0, 1, 2], [0, 1, 2], [16, 16])["q_tile"] == 4
     assert h.plan([0, 2, 3], [0, 1, 2], [16, 16])["q_tile"] == 8
     assert h.plan([0, 300], [0, 20], [16])["kernel"] == lib.KERNEL_MFMA
-    assert h.plan([0, 300, 301], [0, 20, 21], [16, 16])["kernel"] == lib.KERNEL_MIXED
+    # 300 tokens (10 tiles x 320 keys) and a one-token row over 16 keys: tiles only
+    info = h.plan([0, 300, 301], [0, 20, 21], [16, 16])
+    assert info["kernel"] == lib.KERNEL_MFMA and info["q_tile"] == 128
+    # the one-token row over 1200 keys (27 % of 4400): mixed
+    assert h.plan([0, 300, 301], [0, 20, 95], [16, 16])["kernel"] == lib.KERNEL_MIXED
+    # over 1040 keys (24.5 %): tiles
+    assert h.plan([0, 300, 301], [0, 20, 85], [16, 16])["kernel"] == lib.KERNEL_MFMA
 
 
 @pytest.mark.parametrize(

@@ -33,7 +33,7 @@ def handle(h_qo=32, h_kv=8, d=128, P=16, **kw):
         ([0, 1, 2], [0, 3, 5], [16, 4], 16, False, 1, 4),       # decode, g = 4: 4 folded rows
         ([0, 2, 3], [0, 3, 5], [16, 4], 16, True, 1, 8),        # a 2-token row needs the 8-row body
         ([0, 300], [0, 20], [16], 16, False, 2, 0),              # MFMA tiles only
-        ([0, 300, 301], [0, 20, 21], [16, 16], 16, True, 3, 4),  # both bodies
+        ([0, 300, 301], [0, 20, 95], [16, 16], 16, True, 3, 4),  # both bodies (27 % decode-row tokens)
         ([0, 64], [0, 90], [1], 1, False, 2, 0),                 # one key per page: its own instance
     ],
 )
