@@ -163,7 +163,7 @@ int bsr_attn_create(const bsr_attn_config* cfg, int device, bsr_attn_t* out) {
     for (int kind = bsr::kKindDecode; kind <= bsr::kKindMixed; ++kind) {
       for (int ri = 0; ri < 4; ++ri) {
         const bool var = ri >= 2;
-        KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? 0 : (ri % 2 == 0 ? 4 : 8), cap,
+        KernelKey key{kind, bf16, cfg->head_dim, kind == bsr::kKindMfma ? ri % 2 : (ri % 2 == 0 ? 4 : 8), cap,
                       kind == bsr::kKindMfma && cfg->page_size == 1, kv8, var};
         int preferred = 1;
         const void* fn = bsr::find_kernel(key, &preferred);
@@ -311,7 +311,7 @@ static int finish_plan(bsr_attn_t h, std::vector<BlockRow>& rows, int32_t total_
   std::string err;
   int rc = bsr::make_plan(h->pc, rows, total_qo, composable, &res, &err, tree_rows);
   if (rc != BSR_OK) return fail(rc, err);
-  const int rows_key = res.kernel == bsr::kKindMfma ? 0 : res.decode_rows;
+  const int rows_key = res.kernel == bsr::kKindMfma ? (res.short_tile ? 1 : 0) : res.decode_rows;
   const void* fn = nullptr;
   if (h->device >= 0) {
     fn = bsr::find_kernel(KernelKey{res.kernel, h->pc.bf16, h->pc.head_dim, rows_key,

@@ -60,6 +60,17 @@ inline void add_mfma(std::vector<KernelEntry>* out) {
                   kMfmaOcc<D>});
 }
 
+// The 64-row tile at head dim 128 (short query rows: speculative drafts, small
+// prefill chunks): the 16-row body, whose 153 registers per lane allow three
+// workgroups per CU (kernel key rows = 1).
+template <bool CAP, bool PAGE1, bool VAR>
+inline void add_mfma_short(std::vector<KernelEntry>* out) {
+  out->push_back({KernelKey{kKindMfma, true, 128, 1, CAP, PAGE1, false, VAR},
+                  reinterpret_cast<const void*>(
+                      &bsr_persistent_kernel<128, true, 1, kDecodeTb<true>, CAP, kKindMfma, 3, PAGE1, false, VAR>),
+                  3});
+}
+
 // (an FP8 cache's decode body takes four KV rows per lane group and step)
 template <int D, int ROWS, bool CAP, bool VAR, bool KV8 = false>
 inline void add_mixed(std::vector<KernelEntry>* out) {
@@ -95,6 +106,12 @@ inline void register_head_dim(std::vector<KernelEntry>* out) {
   add_decode_kv8<D, 4, true, VAR>(out);
   add_decode_kv8<D, 8, false, VAR>(out);
   add_decode_kv8<D, 8, true, VAR>(out);
+  if constexpr (D == 128) {
+    add_mfma_short<false, false, VAR>(out);
+    add_mfma_short<true, false, VAR>(out);
+    add_mfma_short<false, true, VAR>(out);
+    add_mfma_short<true, true, VAR>(out);
+  }
   if constexpr (D <= 128) {
     // FP8 K/V on the 32-row MFMA body (prefill and wide rows)
     add_mfma<D, false, false, VAR, true>(out);

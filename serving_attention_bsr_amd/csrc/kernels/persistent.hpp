@@ -43,8 +43,10 @@ struct PersistentKernel {
   static_assert(KIND == kKindDecode || !KV8 || D <= 128, "an FP8 K/V cache runs on the 32-row MFMA body only");
   using Decode = DecodeBody<D, BF16, ROWS, TB, CAP, KV8, VAR>;
   // 32 rows per wavefront up to D = 128; 16 rows (two workgroups per CU) at D = 256
-  using Mfma =
-      typename std::conditional<D == 256, MfmaBody16<D, CAP, PAGE1, VAR>, MfmaBody<D, CAP, PAGE1, VAR, KV8>>::type;
+  // (the tile kernel's ROWS = 1 selects the 64-row tile: the 16-row body at D = 128)
+  static constexpr bool kShortTile = KIND == kKindMfma && ROWS == 1;
+  using Mfma = typename std::conditional<D == 256 || kShortTile, MfmaBody16<D, CAP, PAGE1, VAR>,
+                                         MfmaBody<D, CAP, PAGE1, VAR, KV8>>::type;
   using Merge = MergeBody<D, BF16>;
   static constexpr int LDS_FLOATS =
       cmax(Merge::LDS_FLOATS, cmax(KIND == kKindMfma ? 0 : Decode::LDS_FLOATS,
@@ -104,7 +106,8 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
   // another grid is refused as a whole: nothing is written but the status word,
   // which the host's check reports.  This is what a captured launch meets when a
   // later plan needs a different instance.
-  constexpr int32_t kKey = instance_key(KIND, KIND == kKindMfma ? 0 : ROWS, D, BF16, CAP, PAGE1, KV8, VAR);
+  constexpr int32_t kKey =
+      instance_key(KIND, KIND == kKindMfma ? (K::kShortTile ? 1 : 0) : ROWS, D, BF16, CAP, PAGE1, KV8, VAR);
   if (hdr->instance != kKey || hdr->num_wg != static_cast<int32_t>(gridDim.x)) {
     if (wg == 0 && threadIdx.x == 0) status[kStatusWrongKernel] = 1;
     return;

@@ -1,5 +1,5 @@
 // prefill16.hpp -- MFMA attention body with 16 folded rows per wavefront, for
-// head_dim 256.
+// head_dim 256, and for the 64-row tiles of short query rows at head_dim 128.
 //
 // Same method as prefill.hpp (Core mechanisms 3 and 4 of the FlashInfer explainer
 // page, paper sections 3.2 and 3.2.2; GQA folding, paper Appendix A): gathered KV
@@ -60,7 +60,7 @@ struct MfmaBody16 {
   static constexpr int STAGE = 2 * BC * D;  // bf16 elements of one buffer
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LDS_FLOATS = (LDS_BYTES + 3) / 4;
-  static_assert(D == 256, "the 16-row body serves head_dim 256");
+  static_assert(D == 256 || D == 128, "the 16-row body serves head_dim 256, and short tiles at 128");
   static_assert(NI * RPI * kWaves == BC, "whole gather instructions per wavefront");
 
   typedef short i16x4_t __attribute__((ext_vector_type(4)));

@@ -54,7 +54,8 @@ enum StatusWord : int32_t {
 };
 
 // Identity of the persistent-kernel instance a plan is made for: the kernel kind,
-// the decode body's folded rows (0 for the MFMA-only kind), the head dim, the
+// the decode body's folded rows (for the MFMA-only kind: 0 for 128-row tiles, 1
+// for 64-row tiles at head dim 128), the head dim, the
 // handle-level switches that select an instance, and whether the plan carries
 // variant data (ALiBi slopes, tree masks).  The planner writes it into the
 // header and the kernel compares it with its own template arguments, so a launch

@@ -33,7 +33,7 @@ struct KernelKey {
   int kind;  // KernelKind
   bool bf16;
   int head_dim;
-  int rows;  // decode-body folded rows (0 when the kernel has no decode body)
+  int rows;  // decode-body folded rows; tile kernel: 0 = 128-row tile, 1 = 64-row tile (D = 128)
   bool cap;
   bool page1 = false;  // instance specialised for one key per page (MFMA kind only)
   bool kv8 = false;    // K/V are FP8 E4M3 codes, Q/O bf16 (decode kind only)

@@ -463,10 +463,13 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   const int32_t h_kv = cfg.h_kv;
 
   // ---- 1. kernel kind and query tile -----------------------------------------
+  const bool var = !cfg.alibi_raw.empty() || tree_rows != nullptr;
   bool any_decode = false, any_wide = false;
   int64_t max_decode_rows = 0;
   // KV tokens streamed by decode-sized rows and by tiles (once per query tile)
   int64_t decode_kv = 0, tile_kv = 0;
+  // folded rows and count of the rows that need tiles
+  int64_t wide_rows = 0, num_wide = 0;
   const int64_t tile_rows = mfma_tile(cfg.head_dim);
   for (const BlockRow& r : rows) {
     if (r.qo_len == 0) continue;
@@ -478,11 +481,14 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
     } else {
       any_wide = true;
       tile_kv += ceil_div(fr, tile_rows) * r.kv_len;
+      wide_rows += fr;
+      ++num_wide;
     }
   }
   int32_t kernel = kKindDecode;
   int32_t decode_rows = max_decode_rows <= 4 ? 4 : 8;
   int32_t q_tile = decode_rows;
+  bool short_tile = false;
   // the MFMA bodies take bf16 K/V, and FP8 K/V up to head dim 128
   const bool mfma_ok = cfg.bf16 && !(cfg.kv8 && cfg.head_dim > 128);
   if (any_wide) {
@@ -504,9 +510,20 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       // wavefront per SIMD (tree-masked speculative decode, 8 % decode-row tokens:
       // 457 -> 175 us; shared-prefix batch, 35 %: mixed 91 us, tiles 97 us).
       kernel = any_decode && decode_kv * 4 >= decode_kv + tile_kv ? kKindMixed : kKindMfma;
-      // the kernels implement one MFMA tile height per head dim (the smallest tile
-      // at least the mean folded length, from a menu of one)
-      const int32_t tile = mfma_tile(cfg.head_dim);
+      // Tile height: the smallest tile of the menu at least the mean folded length
+      // of the rows that need tiles.  The tile kernel at head dim 128 with bf16 K/V
+      // has two, 64 and 128 rows; every other kernel has one.  The 64-row tile
+      // (16 rows per wavefront, three workgroups per CU) halves the padding of
+      // short rows, such as speculative drafts of 16 tokens at 4 query heads per
+      // KV head (tree-masked decode batch: 176 -> 147 us), and loses to the
+      // 128-row tile on long prefill rows (ragged causal prefill: 1630 ->
+      // 2280 us), whose mean is far above 64.
+      int32_t tile = mfma_tile(cfg.head_dim);
+      if (kernel == kKindMfma && cfg.head_dim == 128 && !cfg.kv8 && g <= kShortTile &&
+          wide_rows <= kShortTile * num_wide && cfg.num_wg[kKindMfma][1][var ? 1 : 0] > 0) {
+        tile = kShortTile;
+        short_tile = true;
+      }
       if (g > tile) {
         *err = "query heads per KV head exceed the MFMA tile height";
         return BSR_ERR_UNSUPPORTED;
@@ -514,8 +531,8 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       q_tile = tile;
     }
   }
-  const bool var = !cfg.alibi_raw.empty() || tree_rows != nullptr;
-  const int32_t nwg = cfg.num_wg[kernel][kernel != kKindMfma && decode_rows == 8 ? 1 : 0][var ? 1 : 0];
+  const int32_t nwg =
+      cfg.num_wg[kernel][(kernel != kKindMfma && decode_rows == 8) || short_tile ? 1 : 0][var ? 1 : 0];
   if (nwg <= 0) {
     *err = "the kernel this plan needs (kind " + std::to_string(kernel) + ") is not built for this handle";
     return BSR_ERR_UNSUPPORTED;
@@ -666,7 +683,7 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   hdr.num_merge = static_cast<int32_t>(tasks.size());
   hdr.num_srcs = static_cast<int32_t>(srcs.size());
   hdr.num_flags = num_flags;
-  hdr.instance = instance_key(kernel, kernel == kKindMfma ? 0 : decode_rows, cfg.head_dim, cfg.bf16, cfg.cap,
+  hdr.instance = instance_key(kernel, kernel == kKindMfma ? (short_tile ? 1 : 0) : decode_rows, cfg.head_dim, cfg.bf16, cfg.cap,
                               kernel == kKindMfma && cfg.page_size == 1, cfg.kv8, var);
   hdr.spin_limit = kDefaultSpinLimit;
   // Claimed items (MFMA tile grids): the tail of each workgroup's queue, the items
@@ -781,6 +798,7 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
   out->num_wg = nwg;
   out->var = var;
   out->q_tile = q_tile;
+  out->short_tile = short_tile;
   out->decode_rows = decode_rows;
   out->num_items = hdr.num_items;
   out->num_partial_items = num_partial_items;

@@ -20,7 +20,8 @@ struct PlanConfig {
   bool causal = false;
   bool bf16 = false;
   bool cap = false;  // logits soft-cap on (selects the kernel instance)
-  // grid per kernel instance: [KernelKind][decode rows 4 -> 0, 8 -> 1][variant data]
+  // grid per kernel instance: [KernelKind][decode rows 4 -> 0, 8 -> 1; tile
+  // kernel: 128-row tile -> 0, 64-row tile -> 1][variant data]
   int32_t num_wg[4][2][2] = {};
   int64_t alpha = 1, beta = 1;
   int64_t gamma = 512;       // fixed cost of a work item or merge task (KV-token units)
@@ -59,6 +60,7 @@ struct PlanResult {
   std::vector<uint8_t> blob;  // the bytes to upload
   int32_t kernel = 0, num_wg = 0, q_tile = 0, decode_rows = 0;
   bool var = false;  // the plan carries variant data (ALiBi slopes, tree masks)
+  bool short_tile = false;  // tile kernel with 64-row tiles at head dim 128
   int32_t num_items = 0, num_partial_items = 0, num_merge = 0, num_srcs = 0;
   int64_t num_partial_rows = 0;
   int64_t kv_chunk = 0, max_wg_cost = 0, total_cost = 0;
@@ -81,6 +83,8 @@ constexpr int kChunkCandidates = 4;
 // MFMA tile height (folded rows) of the kernels: 32 rows per wavefront up to
 // D = 128, 16 rows per wavefront at D = 256.
 inline int32_t mfma_tile(int32_t head_dim) { return head_dim == 256 ? 64 : 128; }
+// The second tile of the tile kernel at D = 128: 16 rows per wavefront.
+constexpr int32_t kShortTile = 64;
 
 // Returns 0 and fills out, or a bsr_status code with a message in err.
 // tree_rows: null, or one 64-bit tree-mask row per query token (rows of block

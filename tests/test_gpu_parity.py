@@ -57,6 +57,30 @@ def test_sweep(case):
     compare(w, o, lse, ro, rl, name)
 
 
+# 64-row tiles at head dim 128 (rows of at most 64 folded rows on average): every
+# instance of the short-tile kernel (soft-cap, one key per page), ragged tiles,
+# causal diagonals, split chunks, decode-sized rows among them
+SHORT = [
+    ("short_d128_causal_p16", [3, 5, 8, 16, 12, 2], [100, 3000, 64, 900, 17, 2], 32, 8, 128, 16, False, 0.0, 0),
+    ("short_d128_g2_p3_split", [20, 31, 5], [700, 31, 2000], 8, 4, 128, 3, True, 0.0, 16),
+    ("short_d128_g8_cap", [8, 3, 6], [1500, 40, 333], 16, 2, 128, 16, False, 25.0, 0),
+    ("short_d128_p1_causal", [16, 9, 4], [2048, 9, 130], 32, 8, 128, 1, True, 0.0, 8),
+    ("short_d128_p1_cap", [11, 16], [90, 4000], 16, 4, 128, 1, True, 30.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", SHORT, ids=[c[0] for c in SHORT])
+def test_short_tiles(case):
+    name, qo, kv, h_qo, h_kv, d, P, causal, cap, nwg = case
+    say("case", name)
+    w = W.build(name, 23, qo, kv, P, h_qo, h_kv, d, dtype="bf16", causal=causal, cap=cap)
+    o, lse, info = run_gpu(w, num_workgroups=nwg)
+    say("plan", info)
+    assert info["q_tile"] == 64 and info["kernel"] == 2
+    ro, rl = oracle_of(w)
+    compare(w, o, lse, ro, rl, name)
+
+
 @pytest.mark.parametrize("name", ["tiny_decode_f32", "batch_decode", "skewed_long_decode", "batch_decode_window"])
 def test_named_decode(name):
     say("workload", name)
