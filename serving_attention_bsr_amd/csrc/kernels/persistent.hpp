@@ -236,6 +236,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
     process(it);
 #ifdef BSR_TRACE
     if (in_pool && threadIdx.x == 0) reinterpret_cast<uint64_t*>(ws + p.trace_off)[wg * 8 + 7] += 1;  // claimed items
+    if (!pooled && qi == ib + 1) BSR_STAMP(7);  // end of the first item (plans without a pool)
 #endif
   }
   BSR_STAMP(1);
