@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
           if (threadIdx.x < 64) {
             for (int32_t k = ib + static_cast<int32_t>(threadIdx.x); k < ie; k += 64) {
               const WorkItem& it = items[k];
-              if (it.flags & kItemPartial)
+              if ((it.flags & (kItemPartial | kItemRelease)) == kItemPartial)
                 __hip_atomic_store(flags + it.flag_id, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
           }
@@ -234,6 +234,14 @@ __global__ __launch_bounds__(kWgThreads, OCC) void bsr_persistent_kernel(RunPara
     part_prev = (it.flags & kItemPartial) != 0;
     flag_prev = it.flag_id;
     process(it);
+    // a queued partial state the plan marks for early release is stamped now
+    // (the same release sequence), so that its merge need not wait for the rest
+    // of this queue (decode and mixed grids; tile grids claim their queue tails)
+    if (KIND != kKindMfma && !in_pool && (it.flags & kItemRelease)) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(flags + it.flag_id, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 #ifdef BSR_TRACE
     if (in_pool && threadIdx.x == 0) reinterpret_cast<uint64_t*>(ws + p.trace_off)[wg * 8 + 7] += 1;  // claimed items
     if (!pooled && qi == ib + 1) BSR_STAMP(7);  // end of the first item (plans without a pool)

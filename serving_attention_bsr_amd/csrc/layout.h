@@ -46,6 +46,7 @@ enum KernelKind : int32_t { kKindDecode = 1, kKindMfma = 2, kKindMixed = 3 };
 enum ItemFlags : int32_t {
   kItemMfma = 1,     // run the MFMA tile body (else the VALU decode body)
   kItemPartial = 2,  // write a partial state to the workspace (else O/LSE directly)
+  kItemRelease = 4,  // stamp the partial state right after the item, not at the end of the queue
 };
 
 enum StatusWord : int32_t {

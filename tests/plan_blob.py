@@ -36,6 +36,7 @@ TASK = np.dtype([("qo_row", "<i4"), ("kv_head", "<i4"), ("src_begin", "<i4"), ("
 SRC = np.dtype([("partial_row", "<i4"), ("flag_id", "<i4")])
 ITEM_MFMA = 1
 ITEM_PARTIAL = 2
+ITEM_RELEASE = 4
 MAGIC = 0x41525342
 
 

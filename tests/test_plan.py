@@ -199,11 +199,14 @@ def test_named_workload_plan_invariants(name, nwg):
             assert n_split_chunks <= 2 * nwg
     assert info["num_partial_items"] == n_split_chunks
     # queues are longest-first (cost = rows + keys + the fixed item cost 512);
-    # with filling, the unsplit units come first, longest first
+    # with filling, the unsplit units come first, longest first; where partial
+    # states are released early, a queue runs its partial items first, and each
+    # part is longest-first
     for wg in range(nwg):
         q_items = items[plan["item_ptr"][wg] : plan["item_ptr"][wg + 1]]
-        if filled:
-            q_items = q_items[(q_items["flags"] & plan_blob.ITEM_PARTIAL) == 0]
+        part = (q_items["flags"] & plan_blob.ITEM_PARTIAL) != 0
+        if filled or (items["flags"] & plan_blob.ITEM_RELEASE).any():
+            q_items = q_items[~part]
         cost = q_items["qo_count"] * g + (q_items["kv_end"] - q_items["kv_begin"]) + 512
         assert np.all(np.diff(cost) <= 0)
     # longest-processing-time bound on the busiest workgroup: attention items by LPT,
@@ -215,8 +218,10 @@ def test_named_workload_plan_invariants(name, nwg):
         max_task = 512 + g * int(plan["merge"]["src_count"].max())
         tasks_per_wg = int(np.diff(plan["merge_ptr"]).max())
         assert info["max_wg_cost"] <= att_bound + tasks_per_wg * max_task
-        # tasks are spread: no workgroup holds two while another holds none
-        if len(plan["merge"]) <= nwg:
+        # tasks are spread: no workgroup holds two while another holds none (when
+        # every partial state is ready only at the end of its queue; states released
+        # early let a workgroup that is idle by then take several)
+        if len(plan["merge"]) <= nwg and not (items["flags"] & plan_blob.ITEM_RELEASE).any():
             assert tasks_per_wg == 1
     else:
         assert info["max_wg_cost"] <= att_bound
