@@ -33,11 +33,13 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <chrono>
 #include <climits>
 #include <cstdint>
 #include <cstring>
 #include <functional>
 #include <queue>
+#include <thread>
 #include <utility>
 
 #include "bsr_attn.h"
@@ -87,14 +89,17 @@ struct Item {
 void assign_longest_first(const std::vector<int64_t>& costs, const std::vector<int32_t>& speed16,
                           std::vector<int64_t>* load, std::vector<int32_t>* owner, std::vector<int32_t>* order) {
   const int32_t n = static_cast<int32_t>(costs.size());
-  order->resize(n);
-  for (int32_t i = 0; i < n; ++i) (*order)[i] = i;
-  std::stable_sort(order->begin(), order->end(),
-                   [&](int32_t a, int32_t b) { return costs[a] > costs[b]; });
+  // longest first, ties in index order: sorted as contiguous (-cost, index) pairs
+  {
+    std::vector<std::pair<int64_t, int32_t>> keyed(n);
+    for (int32_t i = 0; i < n; ++i) keyed[i] = {-costs[i], i};
+    std::sort(keyed.begin(), keyed.end());
+    order->resize(n);
+    for (int32_t i = 0; i < n; ++i) (*order)[i] = keyed[i].second;
+  }
   using Slot = std::pair<int64_t, int32_t>;  // (load, workgroup)
-  using Heap = std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>>;
   std::vector<int32_t> speeds;  // distinct speeds, in first-seen order
-  std::vector<Heap> heaps;
+  std::vector<std::vector<Slot>> heaps;  // binary min-heaps on (load, workgroup)
   for (int32_t w = 0; w < static_cast<int32_t>(load->size()); ++w) {
     size_t k = 0;
     while (k < speeds.size() && speeds[k] != speed16[w]) ++k;
@@ -102,27 +107,43 @@ void assign_longest_first(const std::vector<int64_t>& costs, const std::vector<i
       speeds.push_back(speed16[w]);
       heaps.emplace_back();
     }
-    heaps[k].push({(*load)[w], w});
+    heaps[k].push_back({(*load)[w], w});
   }
+  for (auto& h : heaps) std::make_heap(h.begin(), h.end(), std::greater<Slot>());
+  // the top's load grows: move it down to its place (one pass instead of a pop
+  // and a push)
+  auto sift_down = [](std::vector<Slot>& h) {
+    const size_t m = h.size();
+    size_t i = 0;
+    const Slot v = h[0];
+    while (true) {
+      size_t c = 2 * i + 1;
+      if (c >= m) break;
+      if (c + 1 < m && h[c + 1] < h[c]) ++c;
+      if (!(h[c] < v)) break;
+      h[i] = h[c];
+      i = c;
+    }
+    h[i] = v;
+  };
   owner->assign(n, -1);
   for (int32_t j = 0; j < n; ++j) {
     const int32_t i = (*order)[j];
     size_t best = 0;
     int64_t best_f = INT64_MAX;
     for (size_t k = 0; k < heaps.size(); ++k) {
-      const Slot& top = heaps[k].top();
+      const Slot& top = heaps[k].front();
       const int64_t f = (top.first + costs[i]) * 16 / speeds[k];
-      if (f < best_f || (f == best_f && top.second < heaps[best].top().second)) {
+      if (f < best_f || (f == best_f && top.second < heaps[best].front().second)) {
         best_f = f;
         best = k;
       }
     }
-    Slot s = heaps[best].top();
-    heaps[best].pop();
+    Slot& s = heaps[best].front();
     (*owner)[i] = s.second;
     s.first += costs[i];
     (*load)[s.second] = s.first;
-    heaps[best].push(s);
+    sift_down(heaps[best]);
   }
 }
 
@@ -652,32 +673,79 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       lb_total += cfg.alpha * static_cast<int64_t>(u.nt) * g + cfg.beta * weighted(u, u.l_eff) + cfg.gamma;
   for (int32_t w = 0; w < nwg; ++w) sum_speed16 += speed16[w];
   const int64_t lower_bound = lb_total * 16 / std::max<int64_t>(sum_speed16, 1);
+  // The candidates (chunk length, filling), in scoring order.  The first always
+  // exists; the later ones skip repeats of a chunk length and lengths that cut
+  // nothing (the same plan as the first).
+  struct Candidate {
+    int64_t chunk;
+    bool fill;
+  };
+  std::vector<Candidate> cands;
+  {
+    int64_t last_chunk = -1;
+    for (int k = 1; k <= kChunkCandidates + 2; ++k) {
+      // candidates: the pages' L_kv, L_kv / k (k = 2..), then filling at L_kv and
+      // at L_kv / 2 (the latter cuts units of more than half of L_kv only where a
+      // workgroup's room ends: when more units than workgroups are a little over
+      // L_kv / 2 long, as under a sliding window, whole units cannot balance and
+      // halving every one costs an item and a merge each)
+      const bool fill = k > kChunkCandidates;
+      const int64_t fill_chunk =
+          k == kChunkCandidates + 1 ? base_chunk
+                                    : std::max<int64_t>(round_up(ceil_div(base_chunk, 2), kChunkGranule), min_chunk);
+      int64_t chunk =
+          fill ? fill_chunk : std::max<int64_t>(round_up(ceil_div(base_chunk, k), kChunkGranule), min_chunk);
+      // chunks at least as long as every unit cut nothing: all such candidates,
+      // and filling without long units, are the same plan
+      if (chunk >= max_leff) {
+        if (!cands.empty()) continue;
+        chunk = std::max<int64_t>(round_up(std::max<int64_t>(max_leff, 1), kChunkGranule), base_chunk);
+      }
+      if (!fill && chunk == last_chunk) continue;
+      last_chunk = chunk;
+      cands.push_back({chunk, fill});
+    }
+  }
+  // The first candidate is scored alone: it often ends the search (within 3 % of
+  // the bound).  When it does not and it took long enough to pay for threads, the
+  // others are scored in parallel; either way they are then taken in order with the
+  // same rule, so the plan does not depend on the path.
+  const size_t nc = cands.size();
+  std::vector<Schedule> scored(nc);
+  std::vector<int> rcs(nc, BSR_OK);
+  std::vector<std::string> errs(nc);
+  const auto t_first = std::chrono::steady_clock::now();
+  rcs[0] = schedule(cfg, rows, units, cands[0].chunk, cands[0].fill, nwg, speed16, total_qo, composable, &scored[0],
+                    &errs[0]);
+  const double first_us =
+      std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_first).count();
+  const bool done_early = rcs[0] != BSR_OK || scored[0].makespan * 97 <= lower_bound * 100;
+  if (!done_early && nc > 1) {
+    if (first_us >= cfg.parallel_plan_us && std::thread::hardware_concurrency() > 1) {
+      std::vector<std::thread> pool;
+      pool.reserve(nc - 1);
+      for (size_t c = 1; c < nc; ++c)
+        pool.emplace_back([&, c] {
+          rcs[c] = schedule(cfg, rows, units, cands[c].chunk, cands[c].fill, nwg, speed16, total_qo, composable,
+                            &scored[c], &errs[c]);
+        });
+      for (std::thread& t : pool) t.join();
+    } else {
+      for (size_t c = 1; c < nc; ++c) {
+        rcs[c] = schedule(cfg, rows, units, cands[c].chunk, cands[c].fill, nwg, speed16, total_qo, composable,
+                          &scored[c], &errs[c]);
+        if (rcs[c] != BSR_OK) break;
+      }
+    }
+  }
   Schedule best;
   bool have = false;
-  int64_t last_chunk = -1;
-  for (int k = 1; k <= kChunkCandidates + 2; ++k) {
-    // candidates: the pages' L_kv, L_kv / k (k = 2..), then filling at L_kv and at
-    // L_kv / 2 (the latter cuts units of more than half of L_kv only where a
-    // workgroup's room ends: when more units than workgroups are a little over
-    // L_kv / 2 long, as under a sliding window, whole units cannot balance and
-    // halving every one costs an item and a merge each)
-    const bool fill = k > kChunkCandidates;
-    const int64_t fill_chunk = k == kChunkCandidates + 1
-                                   ? base_chunk
-                                   : std::max<int64_t>(round_up(ceil_div(base_chunk, 2), kChunkGranule), min_chunk);
-    int64_t chunk =
-        fill ? fill_chunk : std::max<int64_t>(round_up(ceil_div(base_chunk, k), kChunkGranule), min_chunk);
-    // chunks at least as long as every unit cut nothing: all such candidates, and
-    // filling without long units, are the same plan
-    if (chunk >= max_leff) {
-      if (have) continue;
-      chunk = std::max<int64_t>(round_up(std::max<int64_t>(max_leff, 1), kChunkGranule), base_chunk);
+  for (size_t c = 0; c < nc; ++c) {
+    if (rcs[c] != BSR_OK) {
+      *err = errs[c];
+      return rcs[c];
     }
-    if (!fill && chunk == last_chunk) continue;
-    last_chunk = chunk;
-    Schedule cand;
-    int rc = schedule(cfg, rows, units, chunk, fill, nwg, speed16, total_qo, composable, &cand, err);
-    if (rc != BSR_OK) return rc;
+    Schedule& cand = scored[c];
     if (!have || cand.makespan * 100 < best.makespan * 97) {
       best = std::move(cand);
       have = true;

@@ -37,6 +37,9 @@ struct PlanConfig {
   int32_t window = 0;  // sliding window in keys (0: none)
   // every item on the workgroup it is assigned to (no run-time claiming)
   bool static_queues = false;
+  // a plan whose first chunking candidate took at least this long (microseconds)
+  // scores the others on threads of their own (the plan is the same either way)
+  double parallel_plan_us = 150.0;
   // ALiBi: per query head, slope / sm_scale (empty: no ALiBi)
   std::vector<float> alibi_raw;
   // capacities (plan rejected beyond them)

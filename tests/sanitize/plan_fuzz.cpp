@@ -123,8 +123,19 @@ int main(int argc, char** argv) {
     }
     PlanResult res;
     std::string err;
+    // every other case scores its candidates on threads whatever their time; the
+    // plan must be the same bytes as the sequential one
+    cfg.parallel_plan_us = 1e12;
     const int rc = make_plan(cfg, rows, total_qo, composable, &res, &err, use_tree ? &tree : nullptr);
     CHECK(rc == BSR_OK || rc == BSR_ERR_UNSUPPORTED || rc == BSR_ERR_CAPACITY);
+    if (c % 2 == 0) {
+      PlanResult par;
+      std::string perr;
+      cfg.parallel_plan_us = 0.0;
+      const int prc = make_plan(cfg, rows, total_qo, composable, &par, &perr, use_tree ? &tree : nullptr);
+      CHECK(prc == rc);
+      CHECK(rc != BSR_OK || par.blob == res.blob);
+    }
     if (rc != BSR_OK) continue;
     ++planned;
     CHECK(res.blob.size() >= sizeof(PlanHeader));

@@ -2,8 +2,10 @@
 
 tests/sanitize/plan_fuzz.cpp drives the planner with random configurations and
 batches (single format and shared-prefix compositions) and checks the structure
-of every plan blob.  It is compiled here with g++ (host code only, no HIP) and
-run; a sanitizer report or a failed structural check fails the test.
+of every plan blob; every other case is planned a second time with its chunking
+candidates scored on threads, which must give the same bytes.  It is compiled
+here with g++ (host code only, no HIP) and run; a sanitizer report or a failed
+check fails the test.
 """
 
 import os
@@ -20,7 +22,7 @@ CSRC = os.path.join(ROOT, "serving_attention_bsr_amd", "csrc")
 def test_planner_under_asan_ubsan(tmp_path):
     exe = str(tmp_path / "plan_fuzz")
     cmd = [
-        "g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+        "g++", "-std=c++17", "-O1", "-g", "-pthread", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
         "-fno-omit-frame-pointer", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
         os.path.join(ROOT, "tests", "sanitize", "plan_fuzz.cpp"), os.path.join(CSRC, "plan.cpp"), "-o", exe,
     ]
