@@ -215,9 +215,30 @@ __global__ __launch_bounds__(kQuestThreads) void quest_select_kernel(const float
     const int shift = 24 - 8 * pass;
     hist[tid] = 0;
     __syncthreads();
-    for (int32_t i = tid; i < m; i += kQuestThreads) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    if (pass == 0) {
+      // Scores of similar size share their top key byte, so on the first digit
+      // most candidates fall into one or two bins and one LDS atomic per key would
+      // serialize on a single address.  Each wavefront instead adds each distinct
+      // bin of its 64 keys once (lanes with the leader's bin found by a ballot).
+      const int lane = tid & 63;
+      for (int32_t i0 = tid - lane; i0 < m; i0 += kQuestThreads) {  // the same for the whole wavefront
+        const int32_t i = i0 + lane;
+        const bool valid = i < m;
+        const uint32_t bin = valid ? keys[i] >> 24 : 0u;
+        uint64_t pending = __ballot(valid);
+        while (pending != 0) {
+          const int leader = __builtin_ctzll(pending);
+          const uint32_t lb = __shfl(bin, leader, 64);
+          const uint64_t same = __ballot(valid && bin == lb);
+          if (lane == leader) atomicAdd(&hist[lb], static_cast<uint32_t>(__builtin_popcountll(same)));
+          pending &= ~same;
+        }
+      }
+    } else {
+      for (int32_t i = tid; i < m; i += kQuestThreads) {
+        const uint32_t key = keys[i];
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     // thread t holds bin 255 - t: its exclusive prefix counts the keys in higher
