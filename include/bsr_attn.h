@@ -188,6 +188,9 @@ int bsr_attn_workspace_size(bsr_attn_t h, size_t* device_bytes, size_t* host_byt
  * the merge map, write the plan into host_staging and enqueue its copy into
  * workspace on stream.  Before rewriting host_staging it waits for the previous
  * copy from it.  Deterministic: the same lengths give the same plan bytes.
+ * When scoring the first chunking takes long (large batches), the other chunkings
+ * are scored on up to five short-lived host threads, joined before the call
+ * returns; the plan is the same either way.
  * Not capturable in a HIP graph.  workspace may be NULL (then nothing is uploaded,
  * and bsr_attn_run keeps launching the last plan that was; required for host-only
  * handles).  Returns BSR_ERR_CAPACITY beyond the maxima,
