@@ -38,6 +38,7 @@
 #include <cstdint>
 #include <cstring>
 #include <functional>
+#include <new>
 #include <queue>
 #include <thread>
 #include <utility>
@@ -721,22 +722,34 @@ int make_plan(const PlanConfig& cfg, const std::vector<BlockRow>& rows, int32_t 
       std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_first).count();
   const bool done_early = rcs[0] != BSR_OK || scored[0].makespan * 97 <= lower_bound * 100;
   if (!done_early && nc > 1) {
-    if (first_us >= cfg.parallel_plan_us && std::thread::hardware_concurrency() > 1) {
-      std::vector<std::thread> pool;
-      pool.reserve(nc - 1);
-      for (size_t c = 1; c < nc; ++c)
-        pool.emplace_back([&, c] {
-          rcs[c] = schedule(cfg, rows, units, cands[c].chunk, cands[c].fill, nwg, speed16, total_qo, composable,
-                            &scored[c], &errs[c]);
-        });
-      for (std::thread& t : pool) t.join();
-    } else {
-      for (size_t c = 1; c < nc; ++c) {
+    // (an allocation failure inside a worker becomes that candidate's error)
+    auto score = [&](size_t c) {
+      try {
         rcs[c] = schedule(cfg, rows, units, cands[c].chunk, cands[c].fill, nwg, speed16, total_qo, composable,
                           &scored[c], &errs[c]);
-        if (rcs[c] != BSR_OK) break;
+      } catch (const std::bad_alloc&) {
+        rcs[c] = BSR_ERR_CAPACITY;
+        errs[c] = "host memory exhausted while scoring a plan";
+      }
+    };
+    size_t threaded = 1;  // candidates 1 .. threaded - 1 run on threads
+    std::vector<std::thread> pool;
+    if (first_us >= cfg.parallel_plan_us && std::thread::hardware_concurrency() > 1) {
+      try {
+        pool.reserve(nc - 1);
+        for (size_t c = 1; c < nc; ++c) {
+          pool.emplace_back(score, c);
+          threaded = c + 1;
+        }
+      } catch (const std::exception&) {
+        // no more threads: the remaining candidates are scored here
       }
     }
+    for (size_t c = threaded; c < nc; ++c) {
+      score(c);
+      if (rcs[c] != BSR_OK) break;
+    }
+    for (std::thread& t : pool) t.join();
   }
   Schedule best;
   bool have = false;
